@@ -1,0 +1,265 @@
+"""Python binding of libbitmoe (routed-MoE + Engram hot path on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libbitmoe.so``; PyTorch supplies device memory and the current stream.  The
+library must have been built (``python -m bit_moe_amd.build``); importing the
+binding does not build it, and every call fails loudly when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitmoe.so")
+
+# status codes / enums (include/bitmoe.h)
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
+MODE_AUTO, MODE_DECODE, MODE_PREFILL = 0, 1, 2
+DEV_BAD_EXPERT, DEV_BAD_ROW = 1, 2
+FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
+
+EXPORTS = [
+    "bitmoe_workspace_size", "moe_route", "moe_expert_ffn", "engram_gather", "moe_plan",
+    "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
+    "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
+]
+
+
+class BitmoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{message} [{code}]")
+        self.code = code
+
+
+class _LayerC(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("shared_wfmt", ctypes.c_int32),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("w_router", ctypes.c_void_p), ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p),
+        ("ws_down", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbitmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libbitmoe.so not built at {path}; run `python -m bit_moe_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    LP = ctypes.POINTER(_LayerC)
+    sig = {
+        "bitmoe_workspace_size": [LP, I32, I32, ctypes.POINTER(SZ)],
+        "moe_route": [LP, P, I32, I32, P, P, P, P, SZ, P],
+        "moe_expert_ffn": [LP, P, I32, I32, P, P, P, I32, I32, P, SZ, P],
+        "engram_gather": [P, I64, P, I64, P, P, P],
+        "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
+        "bitmoe_plan_workspace_size": [I32, I32, I32, ctypes.POINTER(SZ)],
+        "moe_dequant": [P, I32, I64, P, I32, P],
+        "bitmoe_fill": [P, I64, ctypes.c_uint64, I32, P, P],
+        "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.bitmoe_strerror.argtypes = [ctypes.c_int]
+    lib.bitmoe_strerror.restype = ctypes.c_char_p
+    lib.bitmoe_last_error.argtypes = []
+    lib.bitmoe_last_error.restype = ctypes.c_char_p
+    lib.bitmoe_ws_status.argtypes = [P]
+    lib.bitmoe_ws_status.restype = P
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        lib = load()
+        raise BitmoeError(rc, f"{lib.bitmoe_strerror(rc).decode()}: {lib.bitmoe_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, device_only=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if device_only and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class Layer:
+    """One MoE layer whose weights are device tensors (uint8 blocks)."""
+
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    w_gate: torch.Tensor
+    w_up: torch.Tensor
+    w_down: torch.Tensor
+    w_router: torch.Tensor
+    ws_gate: Optional[torch.Tensor] = None
+    ws_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None
+
+    def c(self) -> _LayerC:
+        shared = self.ws_gate is not None
+        return _LayerC(self.d_model, self.d_ff, self.n_experts, self.top_k, WFMT_Q2SB,
+                       WFMT_Q8_0 if shared else WFMT_NONE,
+                       self.w_gate.data_ptr(), self.w_up.data_ptr(), self.w_down.data_ptr(),
+                       self.w_router.data_ptr(),
+                       self.ws_gate.data_ptr() if shared else None,
+                       self.ws_up.data_ptr() if shared else None,
+                       self.ws_down.data_ptr() if shared else None)
+
+
+def workspace_size(layer: Layer, T: int, mode: int = MODE_AUTO) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    lc = layer.c()
+    _check(lib.bitmoe_workspace_size(ctypes.byref(lc), T, mode, ctypes.byref(n)))
+    return n.value
+
+
+def workspace(layer: Layer, T: int, mode: int = MODE_AUTO, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace tensor (its first 256 bytes are the status record)."""
+    return torch.zeros(workspace_size(layer, T, mode), dtype=torch.uint8, device=device)
+
+
+def route(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
+          ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    _require(x, "x")
+    T = x.shape[0]
+    if ids is None:
+        ids = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    _require(ids, "ids", torch.int32)
+    _require(weights, "weights", torch.float32)
+    if bias is not None:
+        _require(bias, "bias", torch.float32)
+    lc = layer.c()
+    _check(lib.moe_route(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids), _ptr(weights),
+                         _ptr(ws), ws.numel(), _stream(stream)))
+    return ids, weights
+
+
+def expert_ffn(layer: Layer, x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, ws: torch.Tensor,
+               y: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16, mode: int = MODE_AUTO, stream=None):
+    lib = load()
+    _require(x, "x")
+    _require(ids, "ids", torch.int32)
+    _require(weights, "weights", torch.float32)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, layer.d_model), dtype=out_dtype, device=x.device)
+    _require(y, "y")
+    lc = layer.c()
+    _check(lib.moe_expert_ffn(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(ids), _ptr(weights), _ptr(y),
+                              _dtype_code(y), mode, _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def engram_gather(table: torch.Tensor, row_ids: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """table [n_rows][264] uint8, row_ids int64 (any shape) -> bf16 bits as int16 [..., 256]."""
+    lib = load()
+    _require(table, "table", torch.uint8)
+    _require(row_ids, "row_ids", torch.int64)
+    n = row_ids.numel()
+    if out is None:
+        out = torch.empty(tuple(row_ids.shape) + (256,), dtype=torch.int16, device=row_ids.device)
+    _require(out, "out")
+    if status is not None:
+        _require(status, "status", torch.int64)
+    _check(lib.engram_gather(_ptr(table), table.numel() // 264, _ptr(row_ids), n, _ptr(out), _ptr(status),
+                             _stream(stream)))
+    return out
+
+
+def plan(ids: torch.Tensor, n_experts: int, status: Optional[torch.Tensor] = None, stream=None) -> dict:
+    lib = load()
+    _require(ids, "ids", torch.int32)
+    T, k = ids.shape
+    dev = ids.device
+    n = ctypes.c_size_t(0)
+    _check(lib.bitmoe_plan_workspace_size(T, k, n_experts, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    out = dict(counts=torch.empty(n_experts, dtype=torch.int32, device=dev),
+               offsets=torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+               perm=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev),
+               union=torch.empty(n_experts, dtype=torch.int32, device=dev),
+               n_union=torch.empty(1, dtype=torch.int32, device=dev))
+    _check(lib.moe_plan(_ptr(ids), T, k, n_experts, _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["perm"]),
+                        _ptr(out["union"]), _ptr(out["n_union"]), _ptr(status), _ptr(ws), ws.numel(),
+                        _stream(stream)))
+    return out
+
+
+def dequant(blocks: torch.Tensor, wfmt: int, n_weights: int, out_dtype=torch.float32, stream=None):
+    lib = load()
+    _require(blocks, "blocks", torch.uint8)
+    out = torch.empty(n_weights, dtype=out_dtype, device=blocks.device)
+    _check(lib.moe_dequant(_ptr(blocks), wfmt, n_weights, _ptr(out), _dtype_code(out), _stream(stream)))
+    return out
+
+
+def fill(dst: torch.Tensor, key: int, kind: int, lut: Optional[torch.Tensor] = None, stream=None):
+    """Fill a uint8 device tensor with the seeded synthetic stream of `key`."""
+    lib = load()
+    _require(dst, "dst", torch.uint8)
+    if lut is not None:
+        _require(lut, "lut", torch.int16)
+    _check(lib.bitmoe_fill(_ptr(dst), dst.numel(), ctypes.c_uint64(key & ((1 << 64) - 1)), kind, _ptr(lut),
+                           _stream(stream)))
+    return dst
+
+
+def read_status(status: torch.Tensor, stream=None):
+    """Synchronise and read a status record -> (code flags, smallest offending index or -1)."""
+    lib = load()
+    code, detail = ctypes.c_int64(0), ctypes.c_int64(0)
+    rc = lib.bitmoe_read_status(_ptr(status), _stream(stream), ctypes.byref(code), ctypes.byref(detail))
+    if rc not in (OK, EDEVICE):
+        _check(rc)
+    return code.value, detail.value
+
+
+def ws_status(ws: torch.Tensor) -> torch.Tensor:
+    """The status record at the start of a layer workspace (int64[2] view)."""
+    return ws[:16].view(torch.int64)

@@ -1,0 +1,377 @@
+// C ABI of libbitmoe: argument validation, workspace carving and kernel
+// dispatch.  Every declaration and its contract is in include/bitmoe.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bitmoe.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(const char *where, hipError_t e) {
+  return fail(BITMOE_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+constexpr int MAX_DECODE_T = 8;
+
+int check_layer(const char *fn, const bitmoe_layer *L) {
+  if (!L) return fail(BITMOE_EINVAL, "%s: layer is NULL", fn);
+  if (L->wfmt != BITMOE_WFMT_Q2SB)
+    return fail(BITMOE_EUNSUPPORTED, "%s: routed weight format %d is not Q2SB (%d)", fn, L->wfmt, BITMOE_WFMT_Q2SB);
+  if (L->shared_wfmt != BITMOE_WFMT_NONE && L->shared_wfmt != BITMOE_WFMT_Q8_0)
+    return fail(BITMOE_EUNSUPPORTED, "%s: shared weight format %d is neither NONE nor Q8_0", fn, L->shared_wfmt);
+  if (!pow2(L->d_model) || L->d_model < 256 || L->d_model > 4096)
+    return fail(BITMOE_EUNSUPPORTED, "%s: d_model %d must be a power of two in [256, 4096]", fn, L->d_model);
+  if (!pow2(L->d_ff) || L->d_ff < 128 || L->d_ff > 4096)
+    return fail(BITMOE_EUNSUPPORTED, "%s: d_ff %d must be a power of two in [128, 4096]", fn, L->d_ff);
+  if (L->n_experts < 1 || L->n_experts > 1024)
+    return fail(BITMOE_EUNSUPPORTED, "%s: n_experts %d outside [1, 1024]", fn, L->n_experts);
+  if (L->top_k < 1 || L->top_k > 8 || L->top_k > L->n_experts)
+    return fail(BITMOE_EINVAL, "%s: top_k %d outside [1, min(8, n_experts=%d)]", fn, L->top_k, L->n_experts);
+  const void *w[3] = {L->w_gate, L->w_up, L->w_down};
+  const char *wn[3] = {"w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 3; ++i)
+    if (!w[i] || !aligned(w[i], 16)) return fail(BITMOE_EINVAL, "%s: %s is NULL or not 16-byte aligned", fn, wn[i]);
+  if (!L->w_router || !aligned(L->w_router, 16))
+    return fail(BITMOE_EINVAL, "%s: w_router is NULL or not 16-byte aligned", fn);
+  if (L->shared_wfmt == BITMOE_WFMT_Q8_0) {
+    const void *s[3] = {L->ws_gate, L->ws_up, L->ws_down};
+    const char *sn[3] = {"ws_gate", "ws_up", "ws_down"};
+    for (int i = 0; i < 3; ++i)
+      if (!s[i] || !aligned(s[i], 16)) return fail(BITMOE_EINVAL, "%s: %s is NULL or not 16-byte aligned", fn, sn[i]);
+  }
+  return BITMOE_OK;
+}
+
+int resolve_mode(int mode, int T) {
+  if (mode == BITMOE_MODE_AUTO) return T <= MAX_DECODE_T ? BITMOE_MODE_DECODE : BITMOE_MODE_PREFILL;
+  return mode;
+}
+
+// Workspace layout (each region 256-byte aligned):
+//   [status record + counters: 256 B][router logits T*E f32][mode-specific]
+struct Carve {
+  size_t off = 0;
+  char *base;
+  explicit Carve(void *b) : base(static_cast<char *>(b)) {}
+  void *take(size_t bytes) {
+    void *p = base ? base + off : nullptr;
+    off += up256(bytes);
+    return p;
+  }
+};
+
+struct DecodeWs {
+  uint16_t *h, *hs, *h_lo, *hs_lo;
+  float *y, *ys;
+};
+
+struct PrefillWs {
+  bm::PlanBufs plan;
+  int32_t *tile_off;
+  uint16_t *xs, *h, *hs;
+  float *y, *ys;
+};
+
+size_t carve_common(Carve &c, const bitmoe_layer *L, int T, int64_t **status, float **logits) {
+  void *st = c.take(256);
+  void *lg = c.take(size_t(T) * L->n_experts * sizeof(float));
+  if (status) *status = static_cast<int64_t *>(st);
+  if (logits) *logits = static_cast<float *>(lg);
+  return c.off;
+}
+
+void carve_decode(Carve &c, const bitmoe_layer *L, int T, DecodeWs *w) {
+  const size_t P = size_t(T) * L->top_k;
+  w->h = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
+  w->hs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
+  w->h_lo = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
+  w->hs_lo = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
+  w->y = static_cast<float *>(c.take(P * L->d_model * 4));
+  w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
+}
+
+void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
+  const int E = L->n_experts;
+  const size_t P = size_t(T) * L->top_k;
+  w->plan.counts = static_cast<int32_t *>(c.take(size_t(E) * 4));
+  w->plan.offsets = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  w->plan.perm = static_cast<int32_t *>(c.take(P * 4));
+  w->plan.union_ids = static_cast<int32_t *>(c.take(size_t(E) * 4));
+  w->plan.n_union = static_cast<int32_t *>(c.take(4));
+  w->plan.chunk_counts = static_cast<int32_t *>(c.take(bm::plan_scratch_bytes(T, E)));
+  w->tile_off = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  w->plan.tile_off = w->tile_off;
+  w->xs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_model * 2));
+  w->h = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
+  w->hs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
+  w->y = static_cast<float *>(c.take(P * L->d_model * 4));
+  w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
+}
+
+size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
+  Carve c(nullptr);
+  carve_common(c, L, T, nullptr, nullptr);
+  if (resolve_mode(mode, T) == BITMOE_MODE_DECODE) {
+    DecodeWs w;
+    carve_decode(c, L, T, &w);
+  } else {
+    PrefillWs w;
+    carve_prefill(c, L, T, &w);
+  }
+  return c.off;
+}
+
+int check_ws(const char *fn, const bitmoe_layer *L, int T, int mode, const void *ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws, 256)) return fail(BITMOE_EINVAL, "%s: workspace is NULL or not 256-byte aligned", fn);
+  const size_t need = ws_bytes_for(L, T, mode);
+  if (ws_bytes < need)
+    return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, need, T);
+  return BITMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *bitmoe_strerror(int code) {
+  switch (code) {
+    case BITMOE_OK: return "BITMOE_OK: success";
+    case BITMOE_EINVAL: return "BITMOE_EINVAL: invalid argument";
+    case BITMOE_EUNSUPPORTED: return "BITMOE_EUNSUPPORTED: unsupported shape or format";
+    case BITMOE_EWORKSPACE: return "BITMOE_EWORKSPACE: workspace too small";
+    case BITMOE_EHIP: return "BITMOE_EHIP: HIP runtime error";
+    case BITMOE_EDEVICE: return "BITMOE_EDEVICE: a device-side fault was recorded";
+    default: return "unknown bitmoe status";
+  }
+}
+
+const char *bitmoe_last_error(void) { return g_last_error; }
+
+int bitmoe_workspace_size(const bitmoe_layer *L, int32_t T, int32_t mode, size_t *bytes) {
+  int rc = check_layer("bitmoe_workspace_size", L);
+  if (rc) return rc;
+  if (!bytes) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: bytes is NULL");
+  if (T < 0) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: T=%d is negative", T);
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL)
+    return fail(BITMOE_EINVAL, "bitmoe_workspace_size: unknown mode %d", mode);
+  *bytes = ws_bytes_for(L, T, mode);
+  return BITMOE_OK;
+}
+
+const int64_t *bitmoe_ws_status(const void *ws) { return static_cast<const int64_t *>(ws); }
+
+int moe_route(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const float *logit_bias,
+              int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const char *fn = "moe_route";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (T == 0) return BITMOE_OK;
+  if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(BITMOE_EINVAL, "%s: topk_ids/topk_w NULL or misaligned", fn);
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(BITMOE_EINVAL, "%s: logit_bias misaligned", fn);
+  // the router needs only the common region of the workspace
+  if (!ws || !aligned(ws, 256)) return fail(BITMOE_EINVAL, "%s: workspace is NULL or not 256-byte aligned", fn);
+  Carve c(ws);
+  int64_t *status;
+  float *logits;
+  carve_common(c, L, T, &status, &logits);
+  if (ws_bytes < c.off)
+    return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, c.off, T);
+  hipError_t e = bm::launch_route(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k, L->w_router,
+                                  logit_bias, logits, topk_ids, topk_w, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const int32_t *topk_ids,
+                   const float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  const char *fn = "moe_expert_ffn";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL) return fail(BITMOE_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (T == 0) return BITMOE_OK;
+  const int m = resolve_mode(mode, T);
+  if (m == BITMOE_MODE_DECODE && T > MAX_DECODE_T)
+    return fail(BITMOE_EUNSUPPORTED, "%s: decode mode takes at most %d tokens, got T=%d", fn, MAX_DECODE_T, T);
+  if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
+  if (!y || !aligned(y, 16)) return fail(BITMOE_EINVAL, "%s: y is NULL or not 16-byte aligned", fn);
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(BITMOE_EINVAL, "%s: topk_ids/topk_w NULL or misaligned", fn);
+  rc = check_ws(fn, L, T, m, ws, ws_bytes);
+  if (rc) return rc;
+  Carve c(ws);
+  int64_t *status;
+  carve_common(c, L, T, &status, nullptr);
+  const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
+  if (m == BITMOE_MODE_DECODE) {
+    DecodeWs w;
+    carve_decode(c, L, T, &w);
+    bm::FfnArgs a{};
+    a.D = L->d_model;
+    a.F = L->d_ff;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.T = T;
+    a.wg = static_cast<const uint8_t *>(L->w_gate);
+    a.wu = static_cast<const uint8_t *>(L->w_up);
+    a.wd = static_cast<const uint8_t *>(L->w_down);
+    a.sg = shared ? static_cast<const uint8_t *>(L->ws_gate) : nullptr;
+    a.su = shared ? static_cast<const uint8_t *>(L->ws_up) : nullptr;
+    a.sd = shared ? static_cast<const uint8_t *>(L->ws_down) : nullptr;
+    a.x = x;
+    a.ids = topk_ids;
+    a.wts = topk_w;
+    a.h = w.h;
+    a.hs = w.hs;
+    a.h_lo = w.h_lo;
+    a.hs_lo = w.hs_lo;
+    a.y = w.y;
+    a.ys = w.ys;
+    a.out = y;
+    a.out_bf16 = y_dtype == BITMOE_BF16;
+    a.status = status;
+    hipError_t e = bm::launch_decode_ffn(a, x_dtype == BITMOE_F32, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return BITMOE_OK;
+  }
+  PrefillWs w;
+  carve_prefill(c, L, T, &w);
+  bm::PrefillArgs a{};
+  a.D = L->d_model;
+  a.F = L->d_ff;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.T = T;
+  a.wg = static_cast<const uint8_t *>(L->w_gate);
+  a.wu = static_cast<const uint8_t *>(L->w_up);
+  a.wd = static_cast<const uint8_t *>(L->w_down);
+  a.sg = shared ? static_cast<const uint8_t *>(L->ws_gate) : nullptr;
+  a.su = shared ? static_cast<const uint8_t *>(L->ws_up) : nullptr;
+  a.sd = shared ? static_cast<const uint8_t *>(L->ws_down) : nullptr;
+  a.x = x;
+  a.x_f32 = x_dtype == BITMOE_F32;
+  a.ids = topk_ids;
+  a.wts = topk_w;
+  a.plan = w.plan;
+  a.plan.status = status;
+  a.tile_off = w.tile_off;
+  a.xs = w.xs;
+  a.h = w.h;
+  a.hs = w.hs;
+  a.y = w.y;
+  a.ys = w.ys;
+  a.out = y;
+  a.out_bf16 = y_dtype == BITMOE_BF16;
+  a.status = status;
+  hipError_t e = bm::launch_prefill_ffn(a, stream);
+  if (e == hipErrorNotSupported) return fail(BITMOE_EUNSUPPORTED, "%s: prefill path not available for this shape", fn);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n, uint16_t *out,
+                  int64_t *status, hipStream_t stream) {
+  const char *fn = "engram_gather";
+  if (n < 0) return fail(BITMOE_EINVAL, "%s: n=%lld is negative", fn, (long long)n);
+  if (n_rows < 0) return fail(BITMOE_EINVAL, "%s: n_rows=%lld is negative", fn, (long long)n_rows);
+  if (n == 0) return BITMOE_OK;
+  if (!table || !aligned(table, 8)) return fail(BITMOE_EINVAL, "%s: table is NULL or not 8-byte aligned", fn);
+  if (!row_ids || !aligned(row_ids, 8)) return fail(BITMOE_EINVAL, "%s: row_ids is NULL or not 8-byte aligned", fn);
+  if (!out || !aligned(out, 16)) return fail(BITMOE_EINVAL, "%s: out is NULL or not 16-byte aligned", fn);
+  if (status && !aligned(status, 8)) return fail(BITMOE_EINVAL, "%s: status not 8-byte aligned", fn);
+  if (n > (int64_t(1) << 33)) return fail(BITMOE_EUNSUPPORTED, "%s: n=%lld rows in one call", fn, (long long)n);
+  hipError_t e = bm::launch_engram_gather(table, n_rows, row_ids, n, out, status, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int bitmoe_plan_workspace_size(int32_t T, int32_t k, int32_t n_experts, size_t *bytes) {
+  if (!bytes || T < 0 || k < 1 || n_experts < 1 || n_experts > 1024)
+    return fail(BITMOE_EINVAL, "bitmoe_plan_workspace_size: bad arguments (T=%d k=%d E=%d)", T, k, n_experts);
+  (void)k;
+  *bytes = up256(bm::plan_scratch_bytes(T, n_experts));
+  return BITMOE_OK;
+}
+
+int moe_plan(const int32_t *topk_ids, int32_t T, int32_t k, int32_t n_experts, int32_t *counts, int32_t *offsets,
+             int32_t *perm, int32_t *union_ids, int32_t *n_union, int64_t *status, void *ws, size_t ws_bytes,
+             hipStream_t stream) {
+  const char *fn = "moe_plan";
+  if (T < 0 || k < 1 || k > 64 || n_experts < 1 || n_experts > 1024)
+    return fail(BITMOE_EINVAL, "%s: bad sizes T=%d k=%d n_experts=%d", fn, T, k, n_experts);
+  if (!counts || !offsets || !n_union || !union_ids) return fail(BITMOE_EINVAL, "%s: NULL output", fn);
+  if (T > 0 && (!topk_ids || !perm)) return fail(BITMOE_EINVAL, "%s: NULL ids or perm", fn);
+  size_t need = up256(bm::plan_scratch_bytes(T, n_experts));
+  if (!ws || ws_bytes < need) return fail(BITMOE_EWORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, ws_bytes, need);
+  bm::PlanBufs p{counts, offsets, perm, union_ids, n_union, static_cast<int32_t *>(ws), nullptr, status};
+  hipError_t e = bm::launch_plan(topk_ids, T, k, n_experts, 0, p, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int moe_dequant(const void *blocks, int32_t wfmt, int64_t n_weights, void *out, int32_t out_dtype,
+                hipStream_t stream) {
+  const char *fn = "moe_dequant";
+  if (wfmt != BITMOE_WFMT_Q2SB && wfmt != BITMOE_WFMT_Q8_0) return fail(BITMOE_EUNSUPPORTED, "%s: format %d", fn, wfmt);
+  if (out_dtype != BITMOE_F32 && out_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: out_dtype %d", fn, out_dtype);
+  const int64_t blk = wfmt == BITMOE_WFMT_Q2SB ? 256 : 32;
+  if (n_weights < 0 || n_weights % blk) return fail(BITMOE_EINVAL, "%s: n_weights %lld not a multiple of %lld", fn,
+                                                    (long long)n_weights, (long long)blk);
+  if (n_weights == 0) return BITMOE_OK;
+  if (!blocks || !aligned(blocks, 4) || !out || !aligned(out, 16))
+    return fail(BITMOE_EINVAL, "%s: NULL or misaligned pointer", fn);
+  hipError_t e = bm::launch_dequant(blocks, wfmt, n_weights, out, out_dtype == BITMOE_BF16, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int bitmoe_fill(void *dst, int64_t n_bytes, uint64_t key, int32_t kind, const uint16_t *lut, hipStream_t stream) {
+  const char *fn = "bitmoe_fill";
+  static const int64_t unit[4] = {1, 84, 34, 264};
+  if (kind < 0 || kind > 3) return fail(BITMOE_EINVAL, "%s: kind %d", fn, kind);
+  if (n_bytes < 0 || n_bytes % unit[kind])
+    return fail(BITMOE_EINVAL, "%s: n_bytes %lld not a multiple of %lld", fn, (long long)n_bytes, (long long)unit[kind]);
+  if (n_bytes == 0) return BITMOE_OK;
+  if (!dst) return fail(BITMOE_EINVAL, "%s: dst is NULL", fn);
+  if ((kind == 1 || kind == 2) && !lut) return fail(BITMOE_EINVAL, "%s: lut is NULL", fn);
+  hipError_t e = bm::launch_fill(dst, n_bytes, key, kind, lut, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int bitmoe_read_status(const int64_t *status, hipStream_t stream, int64_t *code, int64_t *detail) {
+  if (!status || !code || !detail) return fail(BITMOE_EINVAL, "bitmoe_read_status: NULL argument");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail("bitmoe_read_status", e);
+  int64_t h[2];
+  e = hipMemcpy(h, status, sizeof(h), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail("bitmoe_read_status", e);
+  *code = h[0];
+  *detail = h[0] ? INT64_MAX - h[1] : -1;
+  return h[0] ? BITMOE_EDEVICE : BITMOE_OK;
+}
+
+}  // extern "C"

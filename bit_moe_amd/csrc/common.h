@@ -1,0 +1,66 @@
+// Internal helpers shared by the HIP kernels of libbitmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BM_DEVICE __device__ __forceinline__
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+namespace bm {
+
+constexpr int WAVE = 64;
+
+// ---- bf16 ---------------------------------------------------------------
+
+BM_DEVICE float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+BM_DEVICE float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+BM_DEVICE float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float -> bf16 bits, round to nearest even; NaN stays NaN.
+BM_DEVICE uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+BM_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+BM_DEVICE float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+BM_DEVICE float half_to_f32(uint32_t h16) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(h16)));
+}
+
+// ---- reductions -----------------------------------------------------------
+
+template <int WIDTH>
+BM_DEVICE float group_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
+  return v;
+}
+
+BM_DEVICE float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// ---- sticky device status record (int64 code flags, int64 detail) --------
+// detail stores INT64_MAX - index so that atomicMax keeps the smallest index
+// while a zero-filled record means "nothing recorded".
+BM_DEVICE void record_fault(int64_t *status, int64_t flag, int64_t index) {
+  if (!status) return;
+  atomicOr(reinterpret_cast<unsigned long long *>(status), (unsigned long long)flag);
+  atomicMax(reinterpret_cast<unsigned long long *>(status + 1),
+            (unsigned long long)(INT64_MAX - index));
+}
+
+}  // namespace bm

@@ -1,0 +1,76 @@
+// Launch functions of the kernel translation units (internal to libbitmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bm {
+
+hipError_t launch_engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n,
+                                uint16_t *out, int64_t *status, hipStream_t stream);
+hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void *out, int out_bf16,
+                          hipStream_t stream);
+hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const uint16_t *lut,
+                       hipStream_t stream);
+hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr, const float *bias,
+                        float *logits, int32_t *ids, float *wts, hipStream_t stream);
+
+struct PlanBufs {
+  int32_t *counts;
+  int32_t *offsets;
+  int32_t *perm;
+  int32_t *union_ids;
+  int32_t *n_union;
+  int32_t *chunk_counts;
+  int32_t *tile_off;
+  int64_t *status;
+};
+hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, PlanBufs p, hipStream_t stream);
+size_t plan_scratch_bytes(int T, int E);
+
+struct FfnArgs {
+  int D, F, E, k, T;
+  const uint8_t *wg, *wu, *wd;
+  const uint8_t *sg, *su, *sd;
+  const void *x;
+  const int32_t *ids;
+  const float *wts;
+  uint16_t *h;     // [T*k][F] bf16 (hi part in float32 mode)
+  uint16_t *hs;    // [T][F]
+  uint16_t *h_lo;  // float32 mode: lo parts, else unused
+  uint16_t *hs_lo;
+  float *y;
+  float *ys;
+  void *out;
+  int out_bf16;
+  int64_t *status;
+  int chunks_gu, rows_gu;
+  int chunks_dn, rows_dn;
+  int u_max;
+};
+hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream);
+
+struct PrefillArgs {
+  int D, F, E, k, T;
+  const uint8_t *wg, *wu, *wd;
+  const uint8_t *sg, *su, *sd;
+  const void *x;
+  int x_f32;
+  const int32_t *ids;
+  const float *wts;
+  PlanBufs plan;
+  int32_t *tile_off;   // [E+1] M-tiles per expert, prefix
+  uint16_t *xs;        // [T][D] bf16 copy of x (x_f32 only)
+  uint16_t *h;         // [T*k][F] bf16, pair order
+  uint16_t *hs;        // [T][F] bf16
+  float *y;            // [T*k][D] float32, pair order
+  float *ys;           // [T][D]
+  void *out;
+  int out_bf16;
+  int64_t *status;
+};
+hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
+constexpr int PREFILL_BM = 64;  // tokens per M-tile of the grouped GEMM
+
+}  // namespace bm

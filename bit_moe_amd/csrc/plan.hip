@@ -1,0 +1,130 @@
+// Dispatch plan: per-expert counts, exclusive offsets, the pair permutation
+// grouped by expert (stable), the ascending union of selected experts, and
+// the list of M-tiles for the grouped GEMM.
+//
+// "Feature Request: support DeepSeek V4.1 Flash with bounded SSD expert
+// caching", §Stack progress (request-union planning, original-id remaps) and
+// "Strata-DSV4.1", §Latest (10-14) (a verify pass serves the union of its
+// experts once per layer).  Everything stays on the device: no host sync.
+//
+// Three kernels over chunks of 64 tokens (one wave per chunk):
+//  plan_count    per-chunk expert histogram (LDS atomics: counts are
+//                order-independent)
+//  plan_scan     one block: per-expert prefix over chunks, exclusive scan over
+//                experts, union compaction, GEMM tile offsets
+//  plan_scatter  rank of each pair inside its chunk = number of earlier tokens
+//                of the chunk that chose the same expert (a token chooses an
+//                expert at most once), which keeps the order stable.
+#include "common.h"
+#include "internal.h"
+
+namespace bm {
+
+
+__global__ void __launch_bounds__(64) plan_count_kernel(const int32_t *__restrict__ ids, int T, int k, int E,
+                                                        int32_t *__restrict__ chunk_counts, int64_t *status) {
+  extern __shared__ int32_t hist[];  // [E]
+  const int chunk = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 64) hist[e] = 0;
+  __syncthreads();
+  const int t = chunk * 64 + threadIdx.x;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[int64_t(t) * k + j];
+      if (e >= 0 && e < E)
+        atomicAdd(&hist[e], 1);
+      else
+        record_fault(status, 1, int64_t(t) * k + j);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 64) chunk_counts[int64_t(chunk) * E + e] = hist[e];
+}
+
+// One block of 1024 threads.  Thread e owns expert e (E <= 1024).
+__global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, int bm_tile, PlanBufs p) {
+  __shared__ int32_t s_cnt[1024];
+  __shared__ int32_t s_flag[1024];
+  __shared__ int32_t s_tiles[1024];
+  const int e = threadIdx.x;
+  int32_t total = 0;
+  if (e < E) {
+    for (int c = 0; c < n_chunks; ++c) {
+      int32_t *cc = p.chunk_counts + int64_t(c) * E + e;
+      const int32_t v = *cc;
+      *cc = total;  // base of chunk c inside expert e's group
+      total += v;
+    }
+  }
+  s_cnt[e] = e < E ? total : 0;
+  s_flag[e] = (e < E && total > 0) ? 1 : 0;
+  s_tiles[e] = (e < E && bm_tile > 0) ? (total + bm_tile - 1) / bm_tile : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scans over 1024 entries
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t a = 0, b = 0, c = 0;
+    if (e >= o) {
+      a = s_cnt[e - o];
+      b = s_flag[e - o];
+      c = s_tiles[e - o];
+    }
+    __syncthreads();
+    s_cnt[e] += a;
+    s_flag[e] += b;
+    s_tiles[e] += c;
+    __syncthreads();
+  }
+  if (e < E) {
+    p.counts[e] = total;
+    p.offsets[e + 1] = s_cnt[e];
+    if (e == 0) p.offsets[0] = 0;
+    if (total > 0) p.union_ids[s_flag[e] - 1] = e;
+    if (p.tile_off) {
+      p.tile_off[e + 1] = s_tiles[e];
+      if (e == 0) p.tile_off[0] = 0;
+    }
+    if (e == E - 1) *p.n_union = s_flag[e];
+  }
+}
+
+__global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restrict__ ids, int T, int k, int E,
+                                                          PlanBufs p) {
+  extern __shared__ int32_t s_ids[];  // [64 * k]
+  const int chunk = blockIdx.x;
+  const int t0 = chunk * 64;
+  const int nt = min(64, T - t0);
+  for (int i = threadIdx.x; i < nt * k; i += 64) s_ids[i] = ids[int64_t(t0) * k + i];
+  __syncthreads();
+  const int lt = threadIdx.x;
+  if (lt >= nt) return;
+  for (int j = 0; j < k; ++j) {
+    const int e = s_ids[lt * k + j];
+    if (e < 0 || e >= E) continue;
+    int rank = 0;
+    for (int u = 0; u < lt; ++u)
+      for (int jj = 0; jj < k; ++jj) rank += (s_ids[u * k + jj] == e) ? 1 : 0;
+    const int pos = p.offsets[e] + p.chunk_counts[int64_t(chunk) * E + e] + rank;
+    p.perm[pos] = (t0 + lt) * k + j;
+  }
+}
+
+hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, PlanBufs p, hipStream_t stream) {
+  const int n_chunks = (T + 63) / 64;
+  hipLaunchKernelGGL(plan_count_kernel, dim3(n_chunks), dim3(64), E * sizeof(int32_t), stream, ids, T, k, E,
+                     p.chunk_counts, p.status);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_chunks), dim3(64), 64 * k * sizeof(int32_t), stream, ids, T, k,
+                     E, p);
+  return hipGetLastError();
+}
+
+size_t plan_scratch_bytes(int T, int E) {
+  const size_t n_chunks = size_t(T + 63) / 64;
+  return n_chunks * size_t(E) * sizeof(int32_t);
+}
+
+}  // namespace bm

@@ -1,0 +1,132 @@
+// Block dequantisation (checks of the weight decoding) and the seeded synthetic
+// byte streams used to fill large test tensors directly in HBM.
+#include "common.h"
+#include "internal.h"
+
+namespace bm {
+
+// ---- dequantisation -------------------------------------------------------
+// Q2 super-block: w_i = d*scale*q_i - dmin*min.  d*scale, (d*scale)*q and
+// dmin*min are exact in float32 (at most 17 significant bits), so one fused
+// multiply-add gives the single rounding of the exact value.
+
+__global__ void __launch_bounds__(256) dequant_q2_kernel(const uint8_t *__restrict__ blocks, int64_t n_blocks,
+                                                         void *out, int out_bf16) {
+  const int64_t b = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= n_blocks) return;
+  const uint8_t *blk = blocks + b * 84;
+  const float d = half_to_f32(blk[80] | (uint32_t(blk[81]) << 8));
+  const float dmin = half_to_f32(blk[82] | (uint32_t(blk[83]) << 8));
+  float w[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = lane * 4 + r;
+    const uint32_t code = (blk[16 + 32 * (i >> 7) + (i & 31)] >> (2 * ((i & 127) >> 5))) & 3u;
+    const uint32_t s = blk[i >> 4];
+    const float a = d * float(s & 15u);
+    w[r] = __builtin_fmaf(a, float(code), -(dmin * float(s >> 4)));
+  }
+  const int64_t o = b * 256 + lane * 4;
+  if (out_bf16) {
+    uint2 v = make_uint2(pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
+    reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + o)[0] = v;
+  } else {
+    reinterpret_cast<float4 *>(static_cast<float *>(out) + o)[0] = make_float4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+__global__ void __launch_bounds__(256) dequant_q8_kernel(const uint8_t *__restrict__ blocks, int64_t n_weights,
+                                                         void *out, int out_bf16) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= n_weights) return;
+  const uint8_t *blk = blocks + (i >> 5) * 34;
+  const float d = half_to_f32(blk[0] | (uint32_t(blk[1]) << 8));
+  const float w = d * float(int8_t(blk[2 + (i & 31)]));
+  if (out_bf16)
+    static_cast<uint16_t *>(out)[i] = f32_to_bf16(w);
+  else
+    static_cast<float *>(out)[i] = w;
+}
+
+hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void *out, int out_bf16,
+                          hipStream_t stream) {
+  if (n_weights == 0) return hipSuccess;
+  if (wfmt == 1) {
+    const int64_t nb = n_weights / 256;
+    hipLaunchKernelGGL(dequant_q2_kernel, dim3(unsigned((nb + 3) / 4)), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(blocks), nb, out, out_bf16);
+  } else {
+    hipLaunchKernelGGL(dequant_q8_kernel, dim3(unsigned((n_weights + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint8_t *>(blocks), n_weights, out, out_bf16);
+  }
+  return hipGetLastError();
+}
+
+// ---- seeded byte streams (SplitMix64; Steele, Lea & Flood, OOPSLA 2014) ---
+
+BM_DEVICE uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+BM_DEVICE uint64_t stream_word(uint64_t key, int64_t i) {
+  return mix64(key + uint64_t(i + 1) * 0x9E3779B97F4A7C15ull);
+}
+
+BM_DEVICE uint32_t raw_byte(uint64_t key, int64_t i) { return uint32_t(stream_word(key, i) & 0xFFu); }
+
+// kind: 0 raw, 1 Q2 blocks (84 B), 2 Q8_0 blocks (34 B), 3 Engram rows (264 B)
+__global__ void __launch_bounds__(256) fill_kernel(uint8_t *__restrict__ dst, int64_t n_bytes, uint64_t key,
+                                                   int kind, const uint16_t *__restrict__ lut) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_bytes; i += stride) {
+    uint32_t v;
+    if (kind == 1) {
+      const int64_t off = i % 84;
+      if (off >= 80) {
+        const int64_t lo = i - ((off - 80) & 1);  // first byte of the d or dmin field
+        const uint32_t u = raw_byte(key, lo) | (raw_byte(key, lo + 1) << 8);
+        const uint32_t h = lut[u];
+        v = (i == lo) ? (h & 0xFFu) : (h >> 8);
+      } else {
+        v = raw_byte(key, i);
+      }
+    } else if (kind == 2) {
+      const int64_t off = i % 34;
+      if (off < 2) {
+        const int64_t lo = i - off;
+        const uint32_t u = raw_byte(key, lo) | (raw_byte(key, lo + 1) << 8);
+        const uint32_t h = lut[u];
+        v = off == 0 ? (h & 0xFFu) : (h >> 8);
+      } else {
+        v = raw_byte(key, i);
+      }
+    } else if (kind == 3) {
+      const int64_t off = i % 264;
+      const uint64_t H = stream_word(key, i) >> 32;
+      if (off < 256) {
+        const uint32_t c = uint32_t((H * 254ull) >> 32);
+        v = c + (c >= 127u ? 1u : 0u);
+      } else {
+        v = 110u + uint32_t((H * 31ull) >> 32);
+      }
+    } else {
+      v = raw_byte(key, i);
+    }
+    dst[i] = uint8_t(v);
+  }
+}
+
+hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const uint16_t *lut,
+                       hipStream_t stream) {
+  if (n_bytes == 0) return hipSuccess;
+  int64_t blocks = (n_bytes + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<uint8_t *>(dst),
+                     n_bytes, key, kind, lut);
+  return hipGetLastError();
+}
+
+}  // namespace bm

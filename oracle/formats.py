@@ -5,12 +5,12 @@ TEST INFRASTRUCTURE ONLY -- see the package docstring.
 Page citations
 --------------
 * "Feature Request: support DeepSeek V4.1 Flash with bounded SSD expert
-  caching", §Feature Description: experts are stored as "IQ2_XXS gate/up,
-  Q2_K down, Q8_0 attention/shared/head"; Engram rows are 264 bytes, 256 E4M3
-  values plus 8 E8M0 scales.  §Possible Implementation: the rows are decoded
-  "with reference-compatible BF16 rounding".
-* "run the DeepSeek-V4-Flash-Vision tower on CUDA", commit notes: a flat
-  q8_0 block is 34 bytes.
+  caching", §Feature Description: the routed down matrices use Q2_K, the
+  shared expert uses Q8_0; an Engram row is 264 bytes, 256 E4M3 values
+  followed by 8 E8M0 scales.  §Possible Implementation: rows are decoded
+  straight to BF16 with the same rounding as the model's reference.
+* "run the DeepSeek-V4-Flash-Vision tower on CUDA", commit notes: a plain
+  q8_0 block takes 34 bytes.
 
 Readings (the pages name the formats but print no byte layout)
 --------------------------------------------------------------
@@ -64,20 +64,23 @@ def q2_code_location(i: int) -> tuple[int, int]:
     return 16 + 32 * (i // 128) + (i % 32), 2 * ((i % 128) // 32)
 
 
-_Q2_BYTE = np.array([q2_code_location(i)[0] for i in range(256)], dtype=np.int64)
-_Q2_SHIFT = np.array([q2_code_location(i)[1] for i in range(256)], dtype=np.int64)
-
-
 def q2_fields(blocks: np.ndarray):
     """Split [n, 84] uint8 super-blocks into (q[n,256], sc[n,16], m[n,16],
-    d[n], dmin[n]) with d and dmin as exact float64."""
+    d[n], dmin[n]) with d and dmin as exact float64.
+
+    The codes follow :func:`q2_code_location`: the 64 code bytes form two
+    halves of 32; within a half, bit pair s of byte b is weight 32*s + b.
+    """
     blocks = np.asarray(blocks, dtype=np.uint8).reshape(-1, Q2_BLOCK_BYTES)
-    q = (blocks[:, _Q2_BYTE] >> _Q2_SHIFT.astype(np.uint8)) & 3
+    n = blocks.shape[0]
+    qs = blocks[:, 16:80].reshape(n, 2, 1, 32)                 # [block][half][.][byte]
+    shifts = np.array([0, 2, 4, 6], dtype=np.uint8).reshape(1, 1, 4, 1)
+    q = ((qs >> shifts) & 3).reshape(n, 256)                   # [block][128*half + 32*s + byte]
     sc = blocks[:, 0:16] & 0x0F
     m = blocks[:, 0:16] >> 4
     d = half_bits_to_f64(blocks[:, 80].astype(np.uint16) | (blocks[:, 81].astype(np.uint16) << 8))
     dmin = half_bits_to_f64(blocks[:, 82].astype(np.uint16) | (blocks[:, 83].astype(np.uint16) << 8))
-    return q.astype(np.int64), sc.astype(np.int64), m.astype(np.int64), d, dmin
+    return q, sc, m, d, dmin
 
 
 def q2_dequant(blocks: np.ndarray) -> np.ndarray:
@@ -86,8 +89,9 @@ def q2_dequant(blocks: np.ndarray) -> np.ndarray:
     w_i = d*sc_s*q_i - dmin*m_s with s = i // 16 (definition above).
     """
     q, sc, m, d, dmin = q2_fields(blocks)
-    s = np.arange(256) // 16
-    w = d[:, None] * sc[:, s] * q - dmin[:, None] * m[:, s]
+    a = d[:, None] * sc                                          # d*sc per sub-block, exact
+    b = dmin[:, None] * m                                        # dmin*m per sub-block, exact
+    w = np.repeat(a, 16, axis=1) * q - np.repeat(b, 16, axis=1)
     return w.reshape(-1)
 
 

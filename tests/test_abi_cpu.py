@@ -1,0 +1,142 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments synchronously without touching a
+GPU (every call here returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_moe_amd as bm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bm.LIB_PATH):
+        from bit_moe_amd import build
+        build.build()
+    return bm.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("moe_route", "moe_expert_ffn", "engram_gather", "bitmoe_workspace_size"):
+        assert n in names
+    assert sorted(names) == sorted(bm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _layer(**kw):
+    fake = 0x10000  # 16-byte aligned host value; never dereferenced by validation
+    base = dict(d_model=4096, d_ff=2048, n_experts=384, top_k=6, wfmt=bm.WFMT_Q2SB, shared_wfmt=bm.WFMT_Q8_0,
+                w_gate=fake, w_up=fake, w_down=fake, w_router=fake, ws_gate=fake, ws_up=fake, ws_down=fake)
+    base.update(kw)
+    return bm._LayerC(**base)
+
+
+def _ws_size(lib, layer, T, mode=bm.MODE_AUTO):
+    n = ctypes.c_size_t(0)
+    rc = lib.bitmoe_workspace_size(ctypes.byref(layer), T, mode, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_valid_layer(lib):
+    rc, n = _ws_size(lib, _layer(), 1)
+    assert rc == bm.OK and n > 0
+    rc5, n5 = _ws_size(lib, _layer(), 5)
+    assert rc5 == bm.OK and n5 > n
+    rcp, npf = _ws_size(lib, _layer(), 4096)
+    assert rcp == bm.OK and npf > 4096 * 6 * 4096 * 4  # holds the per-pair outputs
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_model", 300, bm.EUNSUPPORTED), ("d_model", 8192, bm.EUNSUPPORTED), ("d_ff", 96, bm.EUNSUPPORTED),
+    ("n_experts", 0, bm.EUNSUPPORTED), ("n_experts", 2000, bm.EUNSUPPORTED), ("top_k", 0, bm.EINVAL),
+    ("top_k", 9, bm.EINVAL), ("wfmt", 7, bm.EUNSUPPORTED), ("shared_wfmt", 5, bm.EUNSUPPORTED),
+    ("w_gate", 0, bm.EINVAL), ("w_up", 0x10004, bm.EINVAL), ("w_router", 0, bm.EINVAL), ("ws_down", 0, bm.EINVAL),
+])
+def test_layer_validation(lib, field, value, code):
+    rc, _ = _ws_size(lib, _layer(**{field: value}), 1)
+    assert rc == code
+    assert lib.bitmoe_last_error().decode()  # a named message
+
+
+def test_topk_above_experts_rejected(lib):
+    rc, _ = _ws_size(lib, _layer(n_experts=4, top_k=6), 1)
+    assert rc == bm.EINVAL and b"top_k" in lib.bitmoe_last_error()
+
+
+def test_route_rejects_bad_args(lib):
+    L = _layer()
+    P = ctypes.c_void_p
+    assert lib.moe_route(None, P(0x10000), bm.BF16, 1, None, P(0x10000), P(0x10000), P(0x10000), 1 << 30,
+                         None) == bm.EINVAL
+    assert lib.moe_route(ctypes.byref(L), None, bm.BF16, 1, None, P(0x10000), P(0x10000), P(0x10000), 1 << 30,
+                         None) == bm.EINVAL
+    assert lib.moe_route(ctypes.byref(L), P(0x10000), 7, 1, None, P(0x10000), P(0x10000), P(0x10000), 1 << 30,
+                         None) == bm.EUNSUPPORTED
+    # workspace too small
+    assert lib.moe_route(ctypes.byref(L), P(0x10000), bm.BF16, 1, None, P(0x10000), P(0x10000), P(0x10000), 64,
+                         None) == bm.EWORKSPACE
+    # empty batch is a no-op
+    assert lib.moe_route(ctypes.byref(L), None, bm.BF16, 0, None, None, None, None, 0, None) == bm.OK
+    assert lib.moe_route(ctypes.byref(L), None, bm.BF16, -1, None, None, None, None, 0, None) == bm.EINVAL
+
+
+def test_expert_ffn_rejects_bad_args(lib):
+    L = _layer()
+    P = ctypes.c_void_p
+    args = lambda **k: [ctypes.byref(L), k.get("x", P(0x10000)), bm.BF16, k.get("T", 1), P(0x10000), P(0x10000),
+                        k.get("y", P(0x10000)), k.get("yd", bm.BF16), k.get("mode", bm.MODE_AUTO),
+                        k.get("ws", P(0x10000)), k.get("wsb", 64), None]
+    assert lib.moe_expert_ffn(*args(y=None, wsb=1 << 40)) == bm.EINVAL
+    assert lib.moe_expert_ffn(*args(yd=9, wsb=1 << 40)) == bm.EUNSUPPORTED
+    assert lib.moe_expert_ffn(*args(mode=5, wsb=1 << 40)) == bm.EINVAL
+    assert lib.moe_expert_ffn(*args(wsb=64)) == bm.EWORKSPACE
+    assert lib.moe_expert_ffn(*args(ws=P(0x10010), wsb=1 << 40)) == bm.EINVAL  # not 256-aligned
+    assert lib.moe_expert_ffn(*args(T=9, mode=bm.MODE_DECODE, wsb=1 << 40)) == bm.EUNSUPPORTED
+    assert lib.moe_expert_ffn(*args(T=0, x=None, y=None)) == bm.OK
+
+
+def test_engram_gather_rejects_bad_args(lib):
+    P = ctypes.c_void_p
+    assert lib.engram_gather(P(0x10000), 10, P(0x10000), 0, None, None, None) == bm.OK  # empty
+    assert lib.engram_gather(None, 10, P(0x10000), 4, P(0x10000), None, None) == bm.EINVAL
+    assert lib.engram_gather(P(0x10004), 10, P(0x10000), 4, P(0x10000), None, None) == bm.EINVAL
+    assert lib.engram_gather(P(0x10000), 10, P(0x10000), 4, P(0x10008), None, None) == bm.EINVAL
+    assert lib.engram_gather(P(0x10000), 10, P(0x10000), -1, P(0x10000), None, None) == bm.EINVAL
+
+
+def test_dequant_and_fill_reject_bad_args(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_dequant(P(0x10000), 9, 256, P(0x10000), bm.F32, None) == bm.EUNSUPPORTED
+    assert lib.moe_dequant(P(0x10000), bm.WFMT_Q2SB, 100, P(0x10000), bm.F32, None) == bm.EINVAL
+    assert lib.moe_dequant(P(0x10000), bm.WFMT_Q8_0, 0, P(0x10000), bm.F32, None) == bm.OK
+    assert lib.bitmoe_fill(P(0x10000), 85, 1, bm.FILL_Q2, P(0x10000), None) == bm.EINVAL
+    assert lib.bitmoe_fill(P(0x10000), 84, 1, bm.FILL_Q2, None, None) == bm.EINVAL
+    assert lib.bitmoe_fill(P(0x10000), 84, 1, 9, None, None) == bm.EINVAL
+
+
+def test_plan_rejects_bad_args(lib):
+    P = ctypes.c_void_p
+    assert lib.moe_plan(P(0x10000), 4, 2, 0, P(1), P(1), P(1), P(1), P(1), None, P(1), 1 << 20, None) == bm.EINVAL
+    assert lib.moe_plan(P(0x10000), 4, 2, 16, None, P(1), P(1), P(1), P(1), None, P(1), 1 << 20, None) == bm.EINVAL
+    assert lib.moe_plan(P(0x10000), 4, 2, 16, P(1), P(1), P(1), P(1), P(1), None, P(1), 0, None) == bm.EWORKSPACE
+
+
+def test_strerror_names_every_code(lib):
+    for code in (bm.OK, bm.EINVAL, bm.EUNSUPPORTED, bm.EWORKSPACE, bm.EHIP, bm.EDEVICE):
+        assert lib.bitmoe_strerror(code).startswith(b"BITMOE_")
