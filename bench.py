@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: one routed-MoE decode layer on one MI355X.
+
+Workload (the single-layer decode configuration): T = 1 token, d_model 4096,
+384 routed experts top-6 (softmax then renormalise), expert FFN width 2048,
+every expert matrix in the 2-bit super-block format, one Q8_0 shared expert,
+bf16 activations.  A step is one pass of the hot path for one token: router
+(logits, top-6, weights) + gate/up GEMV with SwiGLU + down GEMV + combine, all
+HIP kernels of libbitmoe behind its C ABI.
+
+Inputs are seeded and synthetic and resident in HBM before timing.  To keep
+the 256 MB Infinity Cache from serving re-reads, the steps rotate through 16
+independent layer instances (router, experts and shared expert each; about
+51 GB) and every step has a fresh token.
+
+Timed regions (HIP events on the stream the library launches on):
+  1. graph replay of K steps captured in one HIP graph  -> value
+  2. the same K steps launched eagerly with per-kernel event timing
+     -> per-kernel average durations (roofline of the dominant kernel)
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build uses one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode T=1/5), TFLOP/s (prefill)"
+HBM_PEAK_GBPS = 8000.0
+Q2_MAT = 4096 * 2048 // 256 * 84  # 2,752,512 B
+Q8_MAT = 4096 * 2048 // 32 * 34  # 8,912,896 B
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "ffn_gateup_kernel__decode_T1.md")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(T: int, U: int, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
+    """Bytes the method must move per kernel launch (decode path)."""
+    P = T * k
+    return {
+        "router_gemv_kernel": E * D * 4 + T * D * 2 + T * E * 4,
+        "topk_kernel": T * E * 4 + P * 8,
+        "ffn_gateup_kernel": U * 2 * Q2_MAT + 2 * Q8_MAT + T * D * 2 + (P + T) * F * 2,
+        "ffn_down_kernel": U * Q2_MAT + Q8_MAT + (P + T) * F * 2 + (P + T) * D * 4,
+        "combine_kernel": (P + T) * D * 4 + P * 8 + T * D * 2,
+    }
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    text = open(PROFILE_SUMMARY).read()
+    want = source_hash(kernel_src)
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("<!--") and "=" in line:
+            for kv in line.strip("<!-> ").split():
+                if "=" in kv:
+                    a, b = kv.split("=", 1)
+                    vals[a] = b
+    if vals.get("source_sha") != want or "traffic_bytes" not in vals:
+        return None
+    return float(vals["traffic_bytes"])
+
+
+def cpu_baseline(seed: int, n_tokens: int) -> dict:
+    """The fp64 oracle on the host for a bounded sample of decode tokens."""
+    import threadpoolctl
+
+    import synthdata
+    from oracle import moe
+
+    cfg = synthdata.CONFIGS["decode"]
+    ld = synthdata.LayerData(cfg, seed, 0)
+    total = 0.0
+    for t in range(n_tokens):
+        x = ld.x_values(10_000 + t, 1)
+        ids, _, _ = moe.route(x, ld.router(), cfg.top_k)
+        # the layer's inputs (selected experts' bytes) are generated before timing
+        cache = {(kd, int(e)): ld.expert_bytes(kd, int(e)) for e in ids[0] for kd in ("gate", "up", "down")}
+        sh = {kd: ld.shared_bytes(kd) for kd in ("gate", "up", "down")}
+        layer = moe.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, ld.router(),
+                          lambda kd, e: cache[(kd, e)], lambda kd: sh[kd])
+        with threadpoolctl.threadpool_limits(limits=1):  # one core, stated below
+            t0 = time.perf_counter()
+            moe.moe_layer(layer, x)
+            total += time.perf_counter() - t0
+    return {"value": round(n_tokens / total, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens of layer instance 0 (whole fp64 layer: router, 6 experts "
+                      f"dequantised + SwiGLU FFN, Q8_0 shared expert, combine) in {total:.1f} s on one core"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--instances", type=int, default=16)
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this "
+              f"path is a design, not a measured configuration.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_moe_amd as bm
+    import synthdata
+
+    if not os.path.exists(bm.LIB_PATH):
+        from bit_moe_amd import build
+        build.build()
+    bm.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synthdata.CONFIGS["decode"]
+    K, W, NI = args.steps, args.warmup, args.instances
+
+    # ---- inputs, resident in HBM before timing
+    lut = torch.from_numpy(synthdata.half_normal_lut().view(np.int16).copy()).to(dev)
+    layers = []
+    t0 = time.time()
+    for i in range(NI):
+        ld = synthdata.LayerData(cfg, args.seed, i)
+        q2 = []
+        for kind in ("gate", "up", "down"):
+            t = torch.empty(cfg.n_experts * ld.blocks_per_expert * 84, dtype=torch.uint8, device=dev)
+            bm.fill(t, ld.key(kind), bm.FILL_Q2, lut)
+            q2.append(t)
+        q8 = []
+        for kind in ("gate", "up", "down"):
+            t = torch.empty(ld.q8_blocks * 34, dtype=torch.uint8, device=dev)
+            bm.fill(t, ld.shared_key(kind), bm.FILL_Q8, lut)
+            q8.append(t)
+        router = torch.from_numpy(ld.router()).to(dev)
+        layers.append(bm.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, *q2, router, *q8))
+    n_x = K + W
+    xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 1, n_x, cfg.d_model).view(np.int16)).to(dev)
+    xs = xs.view(torch.bfloat16).view(n_x, 1, cfg.d_model)
+    ws = bm.workspace(layers[0], 1)
+    ids = torch.empty((1, cfg.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((1, cfg.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((1, cfg.d_model), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {NI} layer instances resident ({time.time() - t0:.1f} s to generate)")
+
+    def step(i: int) -> None:
+        L = layers[i % NI]
+        x = xs[i]
+        bm.route(L, x, ws, ids=ids, weights=wts)
+        bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=bm.MODE_DECODE)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    # ---- timed region 1: HIP graph replay of K steps
+    graph_ms = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(K):
+                    step(W + i)
+        g.replay()  # warm the graph once
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1)
+        log(f"[bench] graph replay: {graph_ms / K * 1000:.2f} us/step")
+
+    # ---- timed region 2: eager launches with per-kernel HIP event timing
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    bm.profile_start()
+    e0.record()
+    for i in range(K):
+        step(W + i)
+    e1.record()
+    torch.cuda.synchronize()
+    prof = bm.profile_stop()
+    eager_ms = e0.elapsed_time(e1)
+    log(f"[bench] eager: {eager_ms / K * 1000:.2f} us/step")
+
+    T, U = 1, cfg.top_k
+    alg = algorithmic_bytes(T, U)
+    kern = {name: {"avg_us": ms / n * 1000.0, "launches": n,
+                   "alg_bytes": alg.get(name), "gbps": (alg[name] / (ms / n * 1e-3) / 1e9) if name in alg else None}
+            for name, (ms, n) in prof.items()}
+    dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
+    dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
+    achieved = alg[dom] / dom_avg_s / 1e9
+    src = os.path.join(ROOT, "bit_moe_amd", "csrc", "gemv.hip")
+    traffic = stored_traffic(src) if dom == "ffn_gateup_kernel" else None
+
+    step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
+    value = T / (step_ms * 1e-3)
+    step_bytes = sum(alg.values())
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single-layer MoE decode: T=1, d_model 4096, 384 experts top-6, FFN 2048, "
+                               "2-bit super-block experts, Q8_0 shared expert, bf16 activations",
+                   "layer_instances": NI, "timing": "hip graph replay" if graph_ms is not None else "eager"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "hbm_gbps_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        "eager_ms_per_step": round(eager_ms / K, 5),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kern.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

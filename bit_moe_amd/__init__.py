@@ -29,6 +29,7 @@ EXPORTS = [
     "bitmoe_workspace_size", "moe_route", "moe_expert_ffn", "engram_gather", "moe_plan",
     "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
+    "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get",
 ]
 
 
@@ -82,6 +83,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.bitmoe_last_error.restype = ctypes.c_char_p
     lib.bitmoe_ws_status.argtypes = [P]
     lib.bitmoe_ws_status.restype = P
+    lib.bitmoe_profile_start.argtypes = []
+    lib.bitmoe_profile_start.restype = ctypes.c_int
+    lib.bitmoe_profile_stop.argtypes = []
+    lib.bitmoe_profile_stop.restype = ctypes.c_int
+    lib.bitmoe_profile_get.argtypes = [I32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(I64)]
+    lib.bitmoe_profile_get.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -263,3 +271,22 @@ def read_status(status: torch.Tensor, stream=None):
 def ws_status(ws: torch.Tensor) -> torch.Tensor:
     """The status record at the start of a layer workspace (int64[2] view)."""
     return ws[:16].view(torch.int64)
+
+
+def profile_start() -> None:
+    """Start timing every kernel launch of the library with HIP events."""
+    _check(load().bitmoe_profile_start())
+
+
+def profile_stop() -> dict:
+    """Stop timing; returns {kernel name: (total ms, launches)}."""
+    lib = load()
+    n = lib.bitmoe_profile_stop()
+    if n < 0:
+        _check(n)
+    out = {}
+    for i in range(n):
+        name, ms, cnt = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+        _check(lib.bitmoe_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)))
+        out[name.value.decode()] = (ms.value, cnt.value)
+    return out

@@ -526,15 +526,15 @@ static hipError_t launch_decode_nt(const FfnArgs &a, bool xf32, hipStream_t stre
   const int shared_dn = a.sd ? a.chunks_dn : 0;
   dim3 g1(a.u_max * a.chunks_gu + shared_gu), g2(a.u_max * a.chunks_dn + shared_dn);
   if (xf32)
-    hipLaunchKernelGGL((ffn_gateup_kernel<NT, true>), g1, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, true>), g1, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((ffn_gateup_kernel<NT, false>), g1, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, false>), g1, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (xf32)
-    hipLaunchKernelGGL((ffn_down_kernel<NT, true>), g2, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT, true>), g2, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((ffn_down_kernel<NT, false>), g2, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT, false>), g2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -555,7 +555,7 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
     err = launch_decode_nt<NTOK>(a, xf32, stream);
   if (err != hipSuccess) return err;
   const int64_t n4 = int64_t(a.T) * (a.D / 4);
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, a.y, a.sd ? a.ys : nullptr,
+  BM_LAUNCH("combine_kernel", combine_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, a.y, a.sd ? a.ys : nullptr,
                      a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status);
   return hipGetLastError();
 }

@@ -7,6 +7,17 @@
 
 namespace bm {
 
+// Launch-timing hooks (no-ops unless bitmoe_profile_start() was called).
+void prof_begin(const char *name, hipStream_t stream);
+void prof_end(hipStream_t stream);
+
+#define BM_LAUNCH(name, kernel, grid, block, shmem, stream, ...)               \
+  do {                                                                         \
+    ::bm::prof_begin(name, stream);                                            \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
+    ::bm::prof_end(stream);                                                    \
+  } while (0)
+
 hipError_t launch_engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n,
                                 uint16_t *out, int64_t *status, hipStream_t stream);
 hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void *out, int out_bf16,

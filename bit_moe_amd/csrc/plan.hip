@@ -110,14 +110,14 @@ __global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restr
 
 hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, PlanBufs p, hipStream_t stream) {
   const int n_chunks = (T + 63) / 64;
-  hipLaunchKernelGGL(plan_count_kernel, dim3(n_chunks), dim3(64), E * sizeof(int32_t), stream, ids, T, k, E,
+  BM_LAUNCH("plan_count_kernel", plan_count_kernel, dim3(n_chunks), dim3(64), E * sizeof(int32_t), stream, ids, T, k, E,
                      p.chunk_counts, p.status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, p);
+  BM_LAUNCH("plan_scan_kernel", plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(plan_scatter_kernel, dim3(n_chunks), dim3(64), 64 * k * sizeof(int32_t), stream, ids, T, k,
+  BM_LAUNCH("plan_scatter_kernel", plan_scatter_kernel, dim3(n_chunks), dim3(64), 64 * k * sizeof(int32_t), stream, ids, T, k,
                      E, p);
   return hipGetLastError();
 }

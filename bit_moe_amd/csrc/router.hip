@@ -179,19 +179,19 @@ hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, c
   if (T <= 8) {
     dim3 grid((E + 3) / 4);
     if (xbf16)
-      hipLaunchKernelGGL(router_gemv_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
     else
-      hipLaunchKernelGGL(router_gemv_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
   } else {
     dim3 grid((T + 63) / 64, (E + 63) / 64);
     if (xbf16)
-      hipLaunchKernelGGL(router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
     else
-      hipLaunchKernelGGL(router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, ids, wts);
+  BM_LAUNCH("topk_kernel", topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, ids, wts);
   return hipGetLastError();
 }
 

@@ -54,10 +54,10 @@ hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void 
   if (n_weights == 0) return hipSuccess;
   if (wfmt == 1) {
     const int64_t nb = n_weights / 256;
-    hipLaunchKernelGGL(dequant_q2_kernel, dim3(unsigned((nb + 3) / 4)), dim3(256), 0, stream,
+    BM_LAUNCH("dequant_q2_kernel", dequant_q2_kernel, dim3(unsigned((nb + 3) / 4)), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(blocks), nb, out, out_bf16);
   } else {
-    hipLaunchKernelGGL(dequant_q8_kernel, dim3(unsigned((n_weights + 255) / 256)), dim3(256), 0, stream,
+    BM_LAUNCH("dequant_q8_kernel", dequant_q8_kernel, dim3(unsigned((n_weights + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const uint8_t *>(blocks), n_weights, out, out_bf16);
   }
   return hipGetLastError();
@@ -124,7 +124,7 @@ hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const
   if (n_bytes == 0) return hipSuccess;
   int64_t blocks = (n_bytes + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(fill_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<uint8_t *>(dst),
+  BM_LAUNCH("fill_kernel", fill_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, static_cast<uint8_t *>(dst),
                      n_bytes, key, kind, lut);
   return hipGetLastError();
 }

@@ -12,7 +12,7 @@ Sources (web pages on the subject; citations name page and section):
 * "Feature Request: support DeepSeek V4.1 Flash with bounded SSD expert
   caching" (strix-llama.cpp issue 48) -- §Feature Description (Q2_K / Q8_0
   formats, 264-byte Engram rows of 256 E4M3 values + 8 E8M0 scales),
-  §Possible Implementation (reference-compatible BF16 rounding),
+  §Possible Implementation (rows decoded straight to BF16),
   §Engram graph integration, §Runtime stack progress (single expert
   reduction order).
 * "Strata-DSV4.1" README -- §DeepSeek-V4.1-Flash (384 experts, top-6),

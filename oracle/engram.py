@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY -- see the package docstring.
 "Feature Request: support DeepSeek V4.1 Flash with bounded SSD expert
 caching", §Feature Description: a table row is 264 bytes, 256 native E4M3
 values plus 8 E8M0 scales; §Possible Implementation: rows are decoded
-directly with reference-compatible BF16 rounding.
+directly to BF16, rounded the way the model reference rounds.
 
 [Reading: value i uses scale byte 256 + i // 32 (contiguous groups of 32, one
 scale per 32 values); the product E4M3(v) * 2**(E8M0(s) - 127) is rounded
