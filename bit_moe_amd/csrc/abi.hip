@@ -84,7 +84,7 @@ struct DecodeWs {
 struct PrefillWs {
   bm::PlanBufs plan;
   int32_t *tile_off;
-  uint16_t *xs, *h, *hs;
+  uint16_t *xs, *h, *hs, *h_lo, *hs_lo, *sw;
   float *y, *ys;
 };
 
@@ -120,6 +120,11 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   w->xs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_model * 2));
   w->h = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
   w->hs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
+  w->h_lo = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
+  w->hs_lo = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
+  const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
+  // expanded shared expert: bf16 codes (3 matrices) + float scales (one per 32 weights)
+  w->sw = static_cast<uint16_t *>(c.take(shared ? size_t(3) * L->d_ff * L->d_model * (2 + 4 / 32.0) : 0));
   w->y = static_cast<float *>(c.take(P * L->d_model * 4));
   w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
 }
@@ -281,6 +286,9 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   a.xs = w.xs;
   a.h = w.h;
   a.hs = w.hs;
+  a.h_lo = w.h_lo;
+  a.hs_lo = w.hs_lo;
+  a.sw_bf16 = w.sw;
   a.y = w.y;
   a.ys = w.ys;
   a.out = y;

@@ -12,9 +12,11 @@
 //  ffn_gateup_kernel  routed jobs: (union slot, chunk of rows); shared jobs:
 //                     chunk of rows of the Q8_0 shared gate/up.  Every lane
 //                     owns one unit per row and keeps its tokens' activations
-//                     in registers; h = silu(Wg x) * (Wu x) is stored as bf16.
+//                     in registers; h = silu(Wg x) * (Wu x) is stored as a
+//                     bf16 hi + lo pair (h - hi is exact in float32).
 //  ffn_down_kernel    same shape over the down matrices, y = Wd h in float32
-//                     per (token, slot) pair and per token for the shared one.
+//                     per (token, slot) pair and per token for the shared one;
+//                     the hi and lo parts of h are two bf16 operand streams.
 //  combine_kernel     out[t] = sum_j w[t,j] y[t,j] + y_shared[t], j in order,
 //                     rounded once.
 //
@@ -369,9 +371,10 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
         const float hf = silu(gs) * us;
         const uint16_t hv = f32_to_bf16(hf);
         const size_t o = IS_Q8 ? size_t(job.tok[t0 + i]) * a.F + r : size_t(job.pair[t0 + i]) * a.F + r;
+        // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
+        // rounding of h would dominate the layer's output error
         (IS_Q8 ? a.hs : a.h)[o] = hv;
-        // float32 mode keeps h exactly enough as hi + lo bf16 parts
-        if constexpr (XF32) (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
+        (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
       }
     }
   }
@@ -403,9 +406,10 @@ __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
 
 // ---- down -------------------------------------------------------------------
 
-template <int NT, bool XF32, bool IS_Q8>
+template <int NT, bool IS_Q8>
 BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r_begin, int r_end) {
-  constexpr int NV = XF32 ? 2 * NT : NT;
+  constexpr bool XF32 = true;  // h always arrives as hi + lo parts
+  constexpr int NV = 2 * NT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = a.F, LPR = K / 64, RPI = 64 / LPR;
   const int jj = lane % LPR, rsub = lane / LPR;
@@ -453,7 +457,7 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
   }
 }
 
-template <int NT, bool XF32>
+template <int NT>
 __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
   __shared__ int s_bits[32];
   __shared__ Job job;
@@ -471,9 +475,9 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
   for (int t0 = 0; t0 < job.n; t0 += NT) {
     const int nt = min(NT, job.n - t0);
     if (shared)
-      down_rows<NT, XF32, true>(a, job, t0, nt, r_begin, r_end);
+      down_rows<NT, true>(a, job, t0, nt, r_begin, r_end);
     else
-      down_rows<NT, XF32, false>(a, job, t0, nt, r_begin, r_end);
+      down_rows<NT, false>(a, job, t0, nt, r_begin, r_end);
   }
 }
 
@@ -520,21 +524,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 
 // ---- launch -----------------------------------------------------------------
 
-template <int NT>
+template <int NT_GU, int NT_DN>
 static hipError_t launch_decode_nt(const FfnArgs &a, bool xf32, hipStream_t stream) {
   const int shared_gu = a.sg ? a.chunks_gu : 0;
   const int shared_dn = a.sd ? a.chunks_dn : 0;
   dim3 g1(a.u_max * a.chunks_gu + shared_gu), g2(a.u_max * a.chunks_dn + shared_dn);
   if (xf32)
-    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, true>), g1, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_GU, true>), g1, dim3(256), 0, stream, a);
   else
-    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, false>), g1, dim3(256), 0, stream, a);
+    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_GU, false>), g1, dim3(256), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (xf32)
-    BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT, true>), g2, dim3(256), 0, stream, a);
-  else
-    BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT, false>), g2, dim3(256), 0, stream, a);
+  BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT_DN>), g2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -546,17 +547,24 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
   a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
   a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
   a.u_max = min(a.E, a.T * a.k);
+  // tokens held in registers per pass (a job's tokens beyond that take more passes)
   hipError_t err;
   if (a.T == 1)
-    err = launch_decode_nt<1>(a, xf32, stream);
+    err = launch_decode_nt<1, 1>(a, xf32, stream);
   else if (a.T == 2 || xf32)
-    err = launch_decode_nt<2>(a, xf32, stream);
+    err = launch_decode_nt<2, 2>(a, xf32, stream);
   else
-    err = launch_decode_nt<NTOK>(a, xf32, stream);
+    err = launch_decode_nt<NTOK, 2>(a, xf32, stream);
   if (err != hipSuccess) return err;
-  const int64_t n4 = int64_t(a.T) * (a.D / 4);
-  BM_LAUNCH("combine_kernel", combine_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, a.y, a.sd ? a.ys : nullptr,
-                     a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status);
+  return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
+                        stream);
+}
+
+hipError_t launch_combine(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k, int D,
+                          int E, void *out, int out_bf16, int64_t *status, hipStream_t stream) {
+  const int64_t n4 = int64_t(T) * (D / 4);
+  BM_LAUNCH("combine_kernel", combine_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, y, ys, ids, wts,
+            T, k, D, E, out, out_bf16, status);
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ struct FfnArgs {
   int u_max;
 };
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream);
+hipError_t launch_combine(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k, int D,
+                          int E, void *out, int out_bf16, int64_t *status, hipStream_t stream);
 
 struct PrefillArgs {
   int D, F, E, k, T;
@@ -73,8 +75,11 @@ struct PrefillArgs {
   PlanBufs plan;
   int32_t *tile_off;   // [E+1] M-tiles per expert, prefix
   uint16_t *xs;        // [T][D] bf16 copy of x (x_f32 only)
-  uint16_t *h;         // [T*k][F] bf16, pair order
-  uint16_t *hs;        // [T][F] bf16
+  uint16_t *h;         // [T*k][F] bf16 hi part of h, pair order
+  uint16_t *hs;        // [T][F] bf16 hi part (shared expert)
+  uint16_t *h_lo;      // lo parts
+  uint16_t *hs_lo;
+  uint16_t *sw_bf16;   // [3][F*D] bf16 copy of the shared expert (gate, up, down)
   float *y;            // [T*k][D] float32, pair order
   float *ys;           // [T][D]
   void *out;

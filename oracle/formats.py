@@ -89,9 +89,10 @@ def q2_dequant(blocks: np.ndarray) -> np.ndarray:
     w_i = d*sc_s*q_i - dmin*m_s with s = i // 16 (definition above).
     """
     q, sc, m, d, dmin = q2_fields(blocks)
+    n = q.shape[0]
     a = d[:, None] * sc                                          # d*sc per sub-block, exact
     b = dmin[:, None] * m                                        # dmin*m per sub-block, exact
-    w = np.repeat(a, 16, axis=1) * q - np.repeat(b, 16, axis=1)
+    w = q.reshape(n, 16, 16).astype(np.float64) * a[:, :, None] - b[:, :, None]  # sub-block s: weights 16s..16s+15
     return w.reshape(-1)
 
 

@@ -74,12 +74,15 @@ def tensor_key(seed: int, kind: int, layer: int = 0, index: int = 0) -> int:
 
 def words(key: int, start: int, count: int) -> np.ndarray:
     """Words start .. start+count-1 of the stream of ``key`` (uint64)."""
-    i = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    z = np.arange(start + 1, start + count + 1, dtype=np.uint64)
     with np.errstate(over="ignore"):
-        z = np.uint64(key) + i * GAMMA
-        z = (z ^ (z >> np.uint64(30))) * M1
-        z = (z ^ (z >> np.uint64(27))) * M2
-        z = z ^ (z >> np.uint64(31))
+        z *= GAMMA
+        z += np.uint64(key)
+        z ^= z >> np.uint64(30)
+        z *= M1
+        z ^= z >> np.uint64(27)
+        z *= M2
+        z ^= z >> np.uint64(31)
     return z
 
 
