@@ -18,7 +18,9 @@ Timed regions (HIP events on the stream the library launches on):
   2. the same K steps launched eagerly with per-kernel event timing
      -> per-kernel average durations (roofline of the dominant kernel)
 
-Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build uses one GPU.
+Also measured (fields "verify" and "prefill"): the verify batch (T=5) with
+its Engram gathers, and a 4096-token prefill chunk through the grouped-GEMM
+path.  Prints ONE JSON line.  ``--gpus N`` with N > 1 exits: this build uses one GPU.
 """
 from __future__ import annotations
 
@@ -106,6 +108,156 @@ def cpu_baseline(seed: int, n_tokens: int) -> dict:
                       f"dequantised + SwiGLU FFN, Q8_0 shared expert, combine) in {total:.1f} s on one core"}
 
 
+def make_layer(bm, torch, synthdata, cfg, seed: int, layer: int, lut, dev):
+    ld = synthdata.LayerData(cfg, seed, layer)
+    q2 = []
+    for kind in ("gate", "up", "down"):
+        t = torch.empty(cfg.n_experts * ld.blocks_per_expert * 84, dtype=torch.uint8, device=dev)
+        bm.fill(t, ld.key(kind), bm.FILL_Q2, lut)
+        q2.append(t)
+    q8 = []
+    for kind in ("gate", "up", "down"):
+        t = torch.empty(ld.q8_blocks * 34, dtype=torch.uint8, device=dev)
+        bm.fill(t, ld.shared_key(kind), bm.FILL_Q8, lut)
+        q8.append(t)
+    router = torch.from_numpy(ld.router()).to(dev)
+    return bm.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, *q2, router, *q8), ld
+
+
+def time_steps(bm, torch, step, K: int, W: int, graph: bool):
+    """Warm up, then time K steps (graph replay if requested) and K eager steps
+    with per-kernel HIP-event timing.  Returns (graph_ms or None, eager_ms, prof)."""
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    graph_ms = None
+    if graph:
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(K):
+                    step(W + i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1)
+        del g
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    bm.profile_start()
+    e0.record()
+    for i in range(K):
+        step(W + i)
+    e1.record()
+    torch.cuda.synchronize()
+    prof = bm.profile_stop()
+    return graph_ms, e0.elapsed_time(e1), prof
+
+
+def kernel_table(prof: dict, alg: dict, flops: dict = None) -> dict:
+    out = {}
+    for name, (ms, n) in prof.items():
+        avg_s = ms / n * 1e-3
+        row = {"avg_us": round(avg_s * 1e6, 3), "launches": n}
+        if name in alg:
+            row["alg_bytes"] = alg[name]
+            row["gbps"] = round(alg[name] / avg_s / 1e9, 1)
+        if flops and name in flops:
+            row["tflops"] = round(flops[name] / avg_s / 1e12, 1)
+        out[name] = row
+    return out
+
+
+def bench_verify(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """Verify batch (1 token + 4 drafts) through one layer, plus the Engram
+    gather of its 2 x 8 rows per token from two 2^22-row tables."""
+    cfg = synthdata.CONFIGS["verify"]
+    NI = args.instances
+    layers = [make_layer(bm, torch, synthdata, cfg, args.seed, i, lut, dev)[0] for i in range(NI)]
+    tables = []
+    for tb in range(2):
+        t = torch.empty(synthdata.ENGRAM_ROWS * 264, dtype=torch.uint8, device=dev)
+        bm.fill(t, synthdata.tensor_key(args.seed, synthdata.KIND_ENGRAM, tb), bm.FILL_ENGRAM, lut)
+        tables.append(t.view(synthdata.ENGRAM_ROWS, 264))
+    K, W = args.verify_steps, 10
+    T = cfg.T
+    n_seq = K + W
+    toks = synthdata.token_ids(args.seed, 7, n_seq * (T + cfg.history))
+    rid = np.stack([synthdata.engram_row_ids(args.seed, toks[i * (T + cfg.history):(i + 1) * (T + cfg.history)],
+                                             cfg.history) for i in range(n_seq)])  # [n][T][2][8]
+    rid_t = [torch.from_numpy(np.ascontiguousarray(rid[:, :, tb, :])).to(dev) for tb in range(2)]
+    xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 2, n_seq * T, cfg.d_model).view(np.int16)).to(dev)
+    xs = xs.view(torch.bfloat16).view(n_seq, T, cfg.d_model)
+    ws = bm.workspace(layers[0], T)
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, cfg.d_model), dtype=torch.bfloat16, device=dev)
+    rows = [torch.empty((T, 8, 256), dtype=torch.int16, device=dev) for _ in range(2)]
+
+    def step(i):
+        L = layers[i % NI]
+        bm.route(L, xs[i], ws, ids=ids, weights=wts)
+        bm.expert_ffn(L, xs[i], ids, wts, ws, y=y, mode=bm.MODE_DECODE)
+        for tb in range(2):
+            bm.engram_gather(tables[tb], rid_t[tb][i], out=rows[tb])
+
+    graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, not args.no_graph)
+    # union size per timed step (routing recomputed outside the timed regions)
+    U = []
+    for i in range(W, W + K):
+        bm.route(layers[i % NI], xs[i], ws, ids=ids, weights=wts)
+        U.append(len(np.unique(ids.cpu().numpy())))
+    U_mean = float(np.mean(U))
+    step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
+    alg = algorithmic_bytes(T, U_mean)
+    alg["engram_gather_kernel"] = T * 8 * (264 + 512) + T * 8 * 8
+    step_bytes = sum(alg.values()) - alg["engram_gather_kernel"] + 2 * alg["engram_gather_kernel"]
+    return {"workload": "verify batch T=5 (+3 history tokens) through one decode layer, plus 2 x 8 Engram rows "
+                        "per token gathered from two 2^22-row tables",
+            "tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 5),
+            "union_mean": round(U_mean, 2), "hbm_gbps_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+            "eager_ms_per_step": round(eager_ms / K, 5), "kernels": kernel_table(prof, alg)}
+
+
+def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """Prefill chunk T=4096 through one layer with the Zipf router bias."""
+    cfg = synthdata.CONFIGS["prefill"]
+    L, ld = make_layer(bm, torch, synthdata, cfg, args.seed, 0, lut, dev)
+    T, k, D, F = cfg.T, cfg.top_k, cfg.d_model, cfg.d_ff
+    K, W = args.prefill_steps, 2
+    xs = [torch.from_numpy(ld.x(tag).view(np.int16)).to(dev).view(torch.bfloat16) for tag in range(2)]
+    bias = torch.from_numpy(ld.bias()).to(dev)
+    ws = bm.workspace(L, T, bm.MODE_PREFILL)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        x = xs[i % 2]
+        bm.route(L, x, ws, bias=bias, ids=ids, weights=wts)
+        bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=bm.MODE_PREFILL)
+
+    graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, False)
+    step_ms = eager_ms / K
+    routed = 2.0 * T * k * 3 * D * F
+    shared = 2.0 * T * 3 * D * F
+    gemm_ms = prof.get("grouped_gemm_kernel", (0.0, 1))[0] / K
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.n_experts)
+    return {"workload": "prefill chunk T=4096 through one layer (384 experts top-6, Zipf(1.1) router bias "
+                        "lambda=0.3, Q8_0 shared expert)",
+            "tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 4),
+            "tflops_step": round((routed + shared) / (step_ms * 1e-3) / 1e12, 1),
+            "tflops_grouped_gemm": round((routed + shared) / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+            "mfma_bf16_peak_tflops": 2500.0,
+            "expert_tokens": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
+            "kernels": kernel_table(prof, {})}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,8 +266,11 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--verify-steps", type=int, default=200)
+    ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this "
@@ -136,25 +291,11 @@ def main() -> int:
     torch.cuda.set_device(dev)
     cfg = synthdata.CONFIGS["decode"]
     K, W, NI = args.steps, args.warmup, args.instances
-
-    # ---- inputs, resident in HBM before timing
     lut = torch.from_numpy(synthdata.half_normal_lut().view(np.int16).copy()).to(dev)
-    layers = []
+
+    # ---- decode workload: inputs resident in HBM before timing
     t0 = time.time()
-    for i in range(NI):
-        ld = synthdata.LayerData(cfg, args.seed, i)
-        q2 = []
-        for kind in ("gate", "up", "down"):
-            t = torch.empty(cfg.n_experts * ld.blocks_per_expert * 84, dtype=torch.uint8, device=dev)
-            bm.fill(t, ld.key(kind), bm.FILL_Q2, lut)
-            q2.append(t)
-        q8 = []
-        for kind in ("gate", "up", "down"):
-            t = torch.empty(ld.q8_blocks * 34, dtype=torch.uint8, device=dev)
-            bm.fill(t, ld.shared_key(kind), bm.FILL_Q8, lut)
-            q8.append(t)
-        router = torch.from_numpy(ld.router()).to(dev)
-        layers.append(bm.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, *q2, router, *q8))
+    layers = [make_layer(bm, torch, synthdata, cfg, args.seed, i, lut, dev)[0] for i in range(NI)]
     n_x = K + W
     xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 1, n_x, cfg.d_model).view(np.int16)).to(dev)
     xs = xs.view(torch.bfloat16).view(n_x, 1, cfg.d_model)
@@ -163,63 +304,27 @@ def main() -> int:
     wts = torch.empty((1, cfg.top_k), dtype=torch.float32, device=dev)
     y = torch.empty((1, cfg.d_model), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log(f"[bench] {NI} layer instances resident ({time.time() - t0:.1f} s to generate)")
+    log(f"[bench] {NI} decode layer instances resident ({time.time() - t0:.1f} s)")
 
     def step(i: int) -> None:
         L = layers[i % NI]
-        x = xs[i]
-        bm.route(L, x, ws, ids=ids, weights=wts)
-        bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=bm.MODE_DECODE)
+        bm.route(L, xs[i], ws, ids=ids, weights=wts)
+        bm.expert_ffn(L, xs[i], ids, wts, ws, y=y, mode=bm.MODE_DECODE)
 
-    for i in range(W):
-        step(i)
-    torch.cuda.synchronize()
-    log("[bench] warmup done")
-
-    # ---- timed region 1: HIP graph replay of K steps
-    graph_ms = None
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for i in range(K):
-                    step(W + i)
-        g.replay()  # warm the graph once
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_ms = e0.elapsed_time(e1)
-        log(f"[bench] graph replay: {graph_ms / K * 1000:.2f} us/step")
-
-    # ---- timed region 2: eager launches with per-kernel HIP event timing
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    bm.profile_start()
-    e0.record()
-    for i in range(K):
-        step(W + i)
-    e1.record()
-    torch.cuda.synchronize()
-    prof = bm.profile_stop()
-    eager_ms = e0.elapsed_time(e1)
-    log(f"[bench] eager: {eager_ms / K * 1000:.2f} us/step")
+    graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, not args.no_graph)
+    if graph_ms is not None:
+        log(f"[bench] decode graph replay: {graph_ms / K * 1000:.2f} us/step")
+    log(f"[bench] decode eager: {eager_ms / K * 1000:.2f} us/step")
+    del layers
+    torch.cuda.empty_cache()
 
     T, U = 1, cfg.top_k
     alg = algorithmic_bytes(T, U)
-    kern = {name: {"avg_us": ms / n * 1000.0, "launches": n,
-                   "alg_bytes": alg.get(name), "gbps": (alg[name] / (ms / n * 1e-3) / 1e9) if name in alg else None}
-            for name, (ms, n) in prof.items()}
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
     dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
     achieved = alg[dom] / dom_avg_s / 1e9
     src = os.path.join(ROOT, "bit_moe_amd", "csrc", "gemv.hip")
     traffic = stored_traffic(src) if dom == "ffn_gateup_kernel" else None
-
     step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
     value = T / (step_ms * 1e-3)
     step_bytes = sum(alg.values())
@@ -240,13 +345,18 @@ def main() -> int:
                                "2-bit super-block experts, Q8_0 shared expert, bf16 activations",
                    "layer_instances": NI, "timing": "hip graph replay" if graph_ms is not None else "eager"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "hbm_gbps_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(eager_ms / K, 5),
-        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                    for k, v in kern.items()},
+        "kernels": kernel_table(prof, alg),
     }
+    if not args.no_extra:
+        log("[bench] verify workload")
+        out["verify"] = bench_verify(bm, torch, np, synthdata, args, lut, dev)
+        torch.cuda.empty_cache()
+        log("[bench] prefill workload")
+        out["prefill"] = bench_prefill(bm, torch, np, synthdata, args, lut, dev)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
