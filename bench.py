@@ -48,11 +48,15 @@ def log(msg: str) -> None:
 def algorithmic_bytes(T: int, U: int, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
     """Bytes the method must move per kernel launch (decode path)."""
     P = T * k
+    gateup = U * 2 * Q2_MAT + 2 * Q8_MAT + T * D * 2 + (P + T) * F * 2 * 2  # h as bf16 hi + lo
+    down = U * Q2_MAT + Q8_MAT + (P + T) * F * 2 * 2 + (P + T) * D * 4
     return {
         "router_gemv_kernel": E * D * 4 + T * D * 2 + T * E * 4,
         "topk_kernel": T * E * 4 + P * 8,
-        "ffn_gateup_kernel": U * 2 * Q2_MAT + 2 * Q8_MAT + T * D * 2 + (P + T) * F * 2,
-        "ffn_down_kernel": U * Q2_MAT + Q8_MAT + (P + T) * F * 2 + (P + T) * D * 4,
+        "ffn_gateup_kernel": gateup,
+        "ffn_down_kernel": down,
+        "ffn_mfma_gateup_kernel": gateup,
+        "ffn_mfma_down_kernel": down,
         "combine_kernel": (P + T) * D * 4 + P * 8 + T * D * 2,
     }
 
@@ -324,7 +328,7 @@ def main() -> int:
     dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
     achieved = alg[dom] / dom_avg_s / 1e9
     src = os.path.join(ROOT, "bit_moe_amd", "csrc", "gemv.hip")
-    traffic = stored_traffic(src) if dom == "ffn_gateup_kernel" else None
+    traffic = stored_traffic(src) if dom in ("ffn_gateup_kernel", "ffn_mfma_gateup_kernel") else None
     step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
     value = T / (step_ms * 1e-3)
     step_bytes = sum(alg.values())

@@ -29,7 +29,7 @@ EXPORTS = [
     "bitmoe_workspace_size", "moe_route", "moe_expert_ffn", "engram_gather", "moe_plan",
     "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
-    "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get",
+    "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
 ]
 
 
@@ -72,6 +72,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_dequant": [P, I32, I64, P, I32, P],
         "bitmoe_fill": [P, I64, ctypes.c_uint64, I32, P, P],
         "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+        "bitmoe_probe_read": [P, I64, P, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -290,3 +291,8 @@ def profile_stop() -> dict:
         _check(lib.bitmoe_profile_get(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)))
         out[name.value.decode()] = (ms.value, cnt.value)
     return out
+
+
+def probe_read(src: torch.Tensor, n_bytes: int, sink: torch.Tensor, blocks: int, stream=None) -> None:
+    """Enqueue the streaming-read probe over the first n_bytes of src."""
+    _check(load().bitmoe_probe_read(_ptr(src), n_bytes, _ptr(sink), blocks, _stream(stream)))

@@ -370,6 +370,14 @@ int bitmoe_fill(void *dst, int64_t n_bytes, uint64_t key, int32_t kind, const ui
   return BITMOE_OK;
 }
 
+int bitmoe_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, int32_t blocks, hipStream_t stream) {
+  if (!src || !sink || !aligned(src, 16) || n_bytes < 0 || blocks < 1 || blocks > (1 << 20))
+    return fail(BITMOE_EINVAL, "bitmoe_probe_read: bad arguments (n_bytes=%lld blocks=%d)", (long long)n_bytes, blocks);
+  hipError_t e = bm::launch_probe_read(src, n_bytes, sink, blocks, stream);
+  if (e != hipSuccess) return hip_fail("bitmoe_probe_read", e);
+  return BITMOE_OK;
+}
+
 int bitmoe_read_status(const int64_t *status, hipStream_t stream, int64_t *code, int64_t *detail) {
   if (!status || !code || !detail) return fail(BITMOE_EINVAL, "bitmoe_read_status: NULL argument");
   hipError_t e = hipStreamSynchronize(stream);

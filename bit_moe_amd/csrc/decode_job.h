@@ -1,0 +1,52 @@
+// Decode-path job bookkeeping shared by the GEMV and MFMA decode kernels:
+// a routed job is one expert of the ascending union of the call's valid
+// expert ids together with the (token, slot) pairs routed to it; the shared
+// job covers every token.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace bm {
+
+struct Job {
+  int e;           // expert (-1: shared)
+  int n;           // tokens (pairs) of the job, <= 8 (decode takes T <= 8)
+  uint64_t pairs;  // pair indices t*k + j, 8 bits each (shared job: token indices)
+};
+
+// i-th pair / token of a job (shifts instead of array indexing keep the job in
+// registers)
+BM_DEVICE int jpair(const Job &job, int i) { return int((job.pairs >> (8 * i)) & 0xFFu); }
+BM_DEVICE int jtok(const FfnArgs &a, const Job &job, int i) {
+  return job.e < 0 ? jpair(job, i) : jpair(job, i) / a.k;
+}
+
+// Routed job of pair slot p: expert e = ids[p] with every pair routed to it,
+// or false when ids[p] is out of range or an earlier pair already chose e (so
+// each expert of the union is one job and its weights are read once).  All
+// loads are uniform across the block (scalar), no LDS or barrier is needed.
+BM_DEVICE bool pair_job(const FfnArgs &a, int p, Job &job) {
+  const int P = a.T * a.k;
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) return false;
+  job.e = e;
+  job.n = 0;
+  job.pairs = 0;
+  for (int q = 0; q < P; ++q) {
+    if (a.ids[q] != e) continue;
+    if (q < p) return false;  // not the first occurrence
+    if (job.n < 8) job.pairs |= uint64_t(q) << (8 * job.n);
+    ++job.n;
+  }
+  if (job.n > 8) job.n = 8;  // a token picks an expert at most once, so n <= T <= 8
+  return true;
+}
+
+BM_DEVICE void shared_job(const FfnArgs &a, Job &job) {
+  job.e = -1;
+  job.n = a.T;
+  job.pairs = 0x0706050403020100ull;
+}
+
+}  // namespace bm

@@ -32,7 +32,11 @@
 #include "common.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <type_traits>
+
+#include "decode_job.h"
+#include "mfma_q2.h"
 
 namespace bm {
 
@@ -164,14 +168,25 @@ BM_DEVICE void load_xq8_f32(const float *row, int c0, XQ8 &Xh, XQ8 &Xl) {
 
 // ---- one row unit against NV virtual tokens ----------------------------------
 
+struct Q2Unit {  // raw bytes of one lane's quarter super-block
+  u32x4 q;
+  u32x2 sc;
+  uint32_t dd;
+};
+
+BM_DEVICE Q2Unit q2_unit_load(const uint8_t *sb, int h, int p) {
+  Q2Unit r;
+  r.q = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * h + 16 * p);
+  r.sc = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * h);
+  r.dd = *reinterpret_cast<const uint32_t *>(sb + 80);
+  return r;
+}
+
 template <int NV>
-BM_DEVICE void q2_unit_dot(const uint8_t *sb, int h, int p, const XQ2 *X, float *out) {
-  const u32x4 q = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * h + 16 * p);
-  const u32x2 sc = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * h);
-  const uint32_t dd = *reinterpret_cast<const uint32_t *>(sb + 80);
-  const float d = half_to_f32(dd & 0xFFFFu), dmin = half_to_f32(dd >> 16);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  const uint32_t sw0 = sc.x >> (8 * p), sw1 = sc.y >> (8 * p);
+BM_DEVICE void q2_unit_dot(const Q2Unit &u, int p, const XQ2 *X, float *out) {
+  const float d = half_to_f32(u.dd & 0xFFFFu), dmin = half_to_f32(u.dd >> 16);
+  const uint32_t w[4] = {u.q.x, u.q.y, u.q.z, u.q.w};
+  const uint32_t sw0 = u.sc.x >> (8 * p), sw1 = u.sc.y >> (8 * p);
   float yd[NV], ym[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) yd[v] = ym[v] = 0.f;
@@ -210,24 +225,30 @@ BM_DEVICE void q2_unit_dot(const uint8_t *sb, int h, int p, const XQ2 *X, float 
   for (int v = 0; v < NV; ++v) out[v] += d * yd[v] - dmin * ym[v];
 }
 
-template <int NV>
-BM_DEVICE void q8_unit_dot(const uint8_t *u68, const XQ8 *X, float *out) {
-  const u32x4 *p4 = reinterpret_cast<const u32x4 *>(u68);
+struct Q8Unit {  // raw bytes of one lane's two Q8_0 blocks (68 bytes)
   uint32_t dw[17];
+};
+
+BM_DEVICE Q8Unit q8_unit_load(const uint8_t *u68) {
+  Q8Unit r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 v = *reinterpret_cast<const u32x4_a4 *>(u68 + 16 * i);
-    dw[4 * i] = v.x;
-    dw[4 * i + 1] = v.y;
-    dw[4 * i + 2] = v.z;
-    dw[4 * i + 3] = v.w;
+    r.dw[4 * i] = v.x;
+    r.dw[4 * i + 1] = v.y;
+    r.dw[4 * i + 2] = v.z;
+    r.dw[4 * i + 3] = v.w;
   }
-  (void)p4;
-  dw[16] = *reinterpret_cast<const uint32_t *>(u68 + 64);
-  const float dA = half_to_f32(dw[0] & 0xFFFFu), dB = half_to_f32(dw[8] >> 16);
+  r.dw[16] = *reinterpret_cast<const uint32_t *>(u68 + 64);
+  return r;
+}
+
+template <int NV>
+BM_DEVICE void q8_unit_dot(const Q8Unit &u, const XQ8 *X, float *out) {
+  const float dA = half_to_f32(u.dw[0] & 0xFFFFu), dB = half_to_f32(u.dw[8] >> 16);
   uint32_t ux[17];
 #pragma unroll
-  for (int i = 0; i < 17; ++i) ux[i] = dw[i] ^ 0x80808080u;  // q + 128 as unsigned bytes
+  for (int i = 0; i < 17; ++i) ux[i] = u.dw[i] ^ 0x80808080u;  // q + 128 as unsigned bytes
   float acc[2][NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) acc[0][v] = acc[1][v] = 0.f;
@@ -251,60 +272,6 @@ BM_DEVICE void q8_unit_dot(const uint8_t *u68, const XQ8 *X, float *out) {
 // ---- job bookkeeping -------------------------------------------------------
 
 
-struct Job {
-  int e;         // expert (-1: shared)
-  int n;         // tokens (pairs) of the job
-  int tok[64];   // token index
-  int pair[64];  // pair index t*k + j (routed)
-};
-
-// Block prologue: find the expert of routed slot `slot` (ascending union of
-// the valid ids) and its pairs, into LDS.  Returns false when the slot is past
-// the union.  Needs T*k <= blockDim.x.
-BM_DEVICE bool routed_job(const FfnArgs &a, int slot, Job &job, int *s_bits) {
-  const int P = a.T * a.k;
-  const int nwords = (a.E + 31) >> 5;
-  for (int i = threadIdx.x; i < nwords; i += blockDim.x) s_bits[i] = 0;
-  __syncthreads();
-  if (threadIdx.x < P) {
-    const int e = a.ids[threadIdx.x];
-    if (e >= 0 && e < a.E) atomicOr(reinterpret_cast<unsigned *>(&s_bits[e >> 5]), 1u << (e & 31));
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int e = -1, seen = 0;
-    for (int wd = 0; wd < nwords && e < 0; ++wd) {
-      const unsigned bits = unsigned(s_bits[wd]);
-      const int c = __builtin_popcount(bits);
-      if (seen + c > slot) {
-        unsigned b = bits;
-        for (int r = slot - seen; r > 0; --r) b &= b - 1;
-        e = (wd << 5) + __builtin_ctz(b);
-      }
-      seen += c;
-    }
-    job.e = e;
-    job.n = 0;
-    if (e >= 0)
-      for (int p = 0; p < P; ++p)
-        if (a.ids[p] == e) {
-          job.tok[job.n] = p / a.k;
-          job.pair[job.n] = p;
-          ++job.n;
-        }
-  }
-  __syncthreads();
-  return job.e >= 0;
-}
-
-BM_DEVICE void shared_job(const FfnArgs &a, Job &job) {
-  if (threadIdx.x == 0) {
-    job.e = -1;
-    job.n = a.T;
-  }
-  for (int t = threadIdx.x; t < a.T; t += blockDim.x) job.tok[t] = t;
-  __syncthreads();
-}
 
 BM_DEVICE int q2_c0(int n, int q, int K) { return (256 * n + 128 * (q >> 1) + 16 * (q & 1)) % K; }
 
@@ -323,7 +290,7 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
   typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const int t = job.tok[t0 + min(i, nt - 1)];
+    const int t = jtok(a, job, t0 + min(i, nt - 1));
     if constexpr (IS_Q8) {
       if constexpr (XF32)
         load_xq8_f32(static_cast<const float *>(a.x) + size_t(t) * K, c0, X[2 * i], X[2 * i + 1]);
@@ -337,21 +304,39 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
     }
   }
   const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
-  for (int it = wave; it * RPI < r_end - r_begin; it += 4) {
+  using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
+  // raw bytes of the lane's unit in row iteration `it` (software-pipelined one
+  // iteration ahead so the next rows' loads overlap this row's arithmetic)
+  auto load_it = [&](int it, Raw &rg, Raw &ru) {
+    const int r = min(r_begin + it * RPI + rsub, r_end - 1);
+    const int unit = r * LPR + jj;
+    if constexpr (IS_Q8) {
+      rg = q8_unit_load(a.sg + size_t(unit) * 68);
+      ru = q8_unit_load(a.su + size_t(unit) * 68);
+    } else {
+      const int n = unit >> 2, q = unit & 3;
+      rg = q2_unit_load(a.wg + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+      ru = q2_unit_load(a.wu + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+    }
+  };
+  const int n_it = (r_end - r_begin + RPI - 1) / RPI;
+  Raw cg, cu;
+  if (wave < n_it) load_it(wave, cg, cu);
+  for (int it = wave; it < n_it; it += 4) {
+    Raw ng, nu;
+    if (it + 4 < n_it) load_it(it + 4, ng, nu);
     const int r = r_begin + it * RPI + rsub;
     const bool active = r < r_end;
-    const int rr = active ? r : r_begin;
     float g[NV], u[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) g[v] = u[v] = 0.f;
-    const int unit = rr * LPR + jj;
     if constexpr (IS_Q8) {
-      q8_unit_dot<NV>(a.sg + size_t(unit) * 68, X, g);
-      q8_unit_dot<NV>(a.su + size_t(unit) * 68, X, u);
+      q8_unit_dot<NV>(cg, X, g);
+      q8_unit_dot<NV>(cu, X, u);
     } else {
-      const int n = unit >> 2, q = unit & 3;
-      q2_unit_dot<NV>(a.wg + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1, X, g);
-      q2_unit_dot<NV>(a.wu + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1, X, u);
+      const int unit = (active ? r : r_end - 1) * LPR + jj;
+      q2_unit_dot<NV>(cg, unit & 1, X, g);
+      q2_unit_dot<NV>(cu, unit & 1, X, u);
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -370,25 +355,26 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
       if (active && jj == 0 && i < nt) {
         const float hf = silu(gs) * us;
         const uint16_t hv = f32_to_bf16(hf);
-        const size_t o = IS_Q8 ? size_t(job.tok[t0 + i]) * a.F + r : size_t(job.pair[t0 + i]) * a.F + r;
+        const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + i)) * a.F + r : size_t(jpair(job, t0 + i)) * a.F + r;
         // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
         // rounding of h would dominate the layer's output error
         (IS_Q8 ? a.hs : a.h)[o] = hv;
         (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
       }
     }
+    cg = ng;
+    cu = nu;
   }
 }
 
 template <int NT, bool XF32>
 __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
-  __shared__ int s_bits[32];
-  __shared__ Job job;
+  Job job;
   const int n_routed_blocks = a.u_max * a.chunks_gu;
   const bool shared = int(blockIdx.x) >= n_routed_blocks;
   int chunk;
   if (!shared) {
-    if (!routed_job(a, blockIdx.x / a.chunks_gu, job, s_bits)) return;
+    if (!pair_job(a, blockIdx.x / a.chunks_gu, job)) return;
     chunk = blockIdx.x % a.chunks_gu;
   } else {
     shared_job(a, job);
@@ -417,7 +403,7 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
   typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
-    const size_t row = IS_Q8 ? size_t(job.tok[t0 + min(i, nt - 1)]) : size_t(job.pair[t0 + min(i, nt - 1)]);
+    const size_t row = IS_Q8 ? size_t(jtok(a, job, t0 + min(i, nt - 1))) : size_t(jpair(job, t0 + min(i, nt - 1)));
     const uint16_t *hi = (IS_Q8 ? a.hs : a.h) + row * K;
     const uint16_t *lo = (IS_Q8 ? a.hs_lo : a.h_lo) + row * K;
     if constexpr (IS_Q8) {
@@ -429,19 +415,33 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
     }
   }
   const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
-  for (int it = wave; it * RPI < r_end - r_begin; it += 4) {
+  using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
+  auto load_it = [&](int it, Raw &rw) {
+    const int r = min(r_begin + it * RPI + rsub, r_end - 1);
+    const int unit = r * LPR + jj;
+    if constexpr (IS_Q8) {
+      rw = q8_unit_load(a.sd + size_t(unit) * 68);
+    } else {
+      const int n = unit >> 2, q = unit & 3;
+      rw = q2_unit_load(a.wd + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+    }
+  };
+  const int n_it = (r_end - r_begin + RPI - 1) / RPI;
+  Raw cw;
+  if (wave < n_it) load_it(wave, cw);
+  for (int it = wave; it < n_it; it += 4) {
+    Raw nw;
+    if (it + 4 < n_it) load_it(it + 4, nw);
     const int r = r_begin + it * RPI + rsub;
     const bool active = r < r_end;
-    const int rr = active ? r : r_begin;
     float y[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) y[v] = 0.f;
-    const int unit = rr * LPR + jj;
     if constexpr (IS_Q8) {
-      q8_unit_dot<NV>(a.sd + size_t(unit) * 68, X, y);
+      q8_unit_dot<NV>(cw, X, y);
     } else {
-      const int n = unit >> 2, q = unit & 3;
-      q2_unit_dot<NV>(a.wd + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1, X, y);
+      const int unit = (active ? r : r_end - 1) * LPR + jj;
+      q2_unit_dot<NV>(cw, unit & 1, X, y);
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -449,23 +449,23 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
       for (int o = LPR / 2; o > 0; o >>= 1) ys += __shfl_xor(ys, o);
       if (active && jj == 0 && i < nt) {
         if constexpr (IS_Q8)
-          a.ys[size_t(job.tok[t0 + i]) * a.D + r] = ys;
+          a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = ys;
         else
-          a.y[size_t(job.pair[t0 + i]) * a.D + r] = ys;
+          a.y[size_t(jpair(job, t0 + i)) * a.D + r] = ys;
       }
     }
+    cw = nw;
   }
 }
 
 template <int NT>
 __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
-  __shared__ int s_bits[32];
-  __shared__ Job job;
+  Job job;
   const int n_routed_blocks = a.u_max * a.chunks_dn;
   const bool shared = int(blockIdx.x) >= n_routed_blocks;
   int chunk;
   if (!shared) {
-    if (!routed_job(a, blockIdx.x / a.chunks_dn, job, s_bits)) return;
+    if (!pair_job(a, blockIdx.x / a.chunks_dn, job)) return;
     chunk = blockIdx.x % a.chunks_dn;
   } else {
     shared_job(a, job);
@@ -479,6 +479,232 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
     else
       down_rows<NT, false>(a, job, t0, nt, r_begin, r_end);
   }
+}
+
+// ---- routed experts on MFMA (decode) ------------------------------------------
+// Routed jobs: (union slot, 16 output rows).  The 4 waves split the K range
+// (super-blocks) of the block's 16 weight rows and reduce their 16x16 partial
+// tiles in LDS.  The job's tokens (up to np per pass) are staged in LDS with
+// their sub-block sums, so every token of the job uses the same dequantised
+// operands (the union is read once).  Shared-expert blocks (Q8_0) run the GEMV
+// rows of the same kernel launch.
+//
+// GATEUP: A = x (bf16, or float32 split into hi + lo), two weight matrices,
+// SwiGLU epilogue -> h hi/lo.  Down: A = h hi + lo, one matrix -> y float32.
+
+struct MfmaDecodeCfg {
+  int np;     // tokens per pass (LDS rows)
+  int parts;  // 1: A is bf16; 2: A arrives as hi + lo parts
+};
+
+template <bool GATEUP, bool XF32>
+BM_DEVICE void routed_mfma_rows(const FfnArgs &a, const Job &job, int chunk, int np_max, char *smem) {
+  constexpr int PARTS = (GATEUP && !XF32) ? 1 : 2;
+  const int K = GATEUP ? a.D : a.F, N = GATEUP ? a.F : a.D;
+  const int nsb = K / 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, nl = lane & 15, p = g & 1;
+  const int r0 = chunk * 16, n = r0 + nl;
+  // LDS carve: A parts, sub-block sums, sc tables, reduction tiles
+  uint16_t *As = reinterpret_cast<uint16_t *>(smem);
+  uint16_t *Al = As + size_t(np_max) * K;
+  uint16_t *Xs = As + size_t(PARTS) * np_max * K;             // [np][nsb][32]
+  uint2 *tab = reinterpret_cast<uint2 *>(Xs + size_t(np_max) * nsb * 32);
+  float *red = reinterpret_cast<float *>(tab + 16);            // [4][2][256]
+  if (tid < 16) tab[tid] = sc_table_entry(tid);
+  const size_t mat_bytes = size_t(a.F) * a.D / 256 * 84;
+  const uint8_t *w0 = (GATEUP ? a.wg : a.wd) + size_t(job.e) * mat_bytes + size_t(n) * (K / 256) * 84;
+  const uint8_t *w1 = GATEUP ? a.wu + size_t(job.e) * mat_bytes + size_t(n) * (K / 256) * 84 : nullptr;
+  const int sb0 = wave * nsb / 4, sb1 = (wave + 1) * nsb / 4;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  // two super-blocks of weights in flight per wave (current + next), the first
+  // two issued before the activations are staged
+  Q2Raw c0, c1, n0, n1;
+  auto load_sb = [&](int sb, Q2Raw &r0, Q2Raw &r1) {
+    r0 = q2_load(w0 + size_t(sb) * 84, g);
+    if constexpr (GATEUP) r1 = q2_load(w1 + size_t(sb) * 84, g);
+  };
+  if (sb0 < sb1) load_sb(sb0, c0, c1);
+  if (sb0 + 1 < sb1) load_sb(sb0 + 1, n0, n1);
+
+  for (int t0 = 0; t0 < job.n; t0 += np_max) {
+    const int np = min(np_max, job.n - t0);
+    __syncthreads();  // LDS of the previous pass is consumed
+    // stage the A rows (8 bf16 per thread-iteration)
+    const int k8 = K / 8;
+    for (int idx = tid; idx < np * k8; idx += 256) {
+      const int row = idx / k8, c = (idx % k8) * 8;
+      uint4 hi, lo = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (GATEUP) {
+        const int tok = jtok(a, job, t0 + row);
+        if constexpr (XF32) {
+          const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + size_t(tok) * K + c);
+          const float4 f0 = src[0], f1 = src[1];
+          const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+          uint32_t hb[8], lb[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            hb[i] = f32_to_bf16(f[i]);
+            lb[i] = f32_to_bf16(f[i] - bf16_to_f32(uint16_t(hb[i])));
+          }
+          hi = make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
+          lo = make_uint4(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16);
+        } else {
+          hi = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + size_t(tok) * K + c);
+        }
+      } else {
+        const size_t pr = size_t(jpair(job, t0 + row));
+        hi = *reinterpret_cast<const uint4 *>(a.h + pr * K + c);
+        lo = *reinterpret_cast<const uint4 *>(a.h_lo + pr * K + c);
+      }
+      *reinterpret_cast<uint4 *>(As + size_t(row) * K + c) = hi;
+      if constexpr (PARTS == 2) *reinterpret_cast<uint4 *>(Al + size_t(row) * K + c) = lo;
+    }
+    __syncthreads();
+    // sub-block sums of the staged rows (hi + lo), split into bf16 hi + lo
+    const int k16 = K / 16;
+    for (int idx = tid; idx < np * k16; idx += 256) {
+      const int row = idx / k16, sbk = idx % k16;
+      const uint16_t *src = As + size_t(row) * K + sbk * 16;
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += bf16_to_f32(src[i]);
+      if constexpr (PARTS == 2) {
+        const uint16_t *sl = Al + size_t(row) * K + sbk * 16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += bf16_to_f32(sl[i]);
+      }
+      const uint16_t shi = f32_to_bf16(sum);
+      uint16_t *dst = Xs + (size_t(row) * nsb + (sbk >> 4)) * 32;
+      dst[q2_sum_slot(sbk & 15, 0)] = shi;
+      dst[q2_sum_slot(sbk & 15, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
+    }
+    __syncthreads();
+    // this wave's super-blocks
+    const bool arow = nl < np;  // lane supplies A row nl
+    f32x4_t acc0 = zero, acc1 = zero;
+    if (t0 > 0 && sb0 < sb1) {  // another pass over the same rows: reload the pipeline
+      load_sb(sb0, c0, c1);
+      if (sb0 + 1 < sb1) load_sb(sb0 + 1, n0, n1);
+    }
+    for (int sb = sb0; sb < sb1; ++sb) {
+      const Q2Raw r0w = c0;
+      const Q2Raw r1w = c1;
+      c0 = n0;
+      c1 = n1;
+      if (sb + 2 < sb1) load_sb(sb + 2, n0, n1);
+      f32x4_t cm0 = zero, cm1 = zero;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int kk = sb * 256 + q2_kofs(t, g);
+        uint32_t A[4] = {0u, 0u, 0u, 0u}, B0[4], B1[4];
+        if (arow) ld16(As + size_t(nl) * K + kk, A);
+        q2_main_operand(r0w, p, t, tab, B0);
+        cm0 = mfma16(A, B0, cm0);
+        if constexpr (GATEUP) {
+          q2_main_operand(r1w, p, t, tab, B1);
+          cm1 = mfma16(A, B1, cm1);
+        }
+        if constexpr (PARTS == 2) {
+          if (arow) ld16(Al + size_t(nl) * K + kk, A);
+          cm0 = mfma16(A, B0, cm0);
+          if constexpr (GATEUP) cm1 = mfma16(A, B1, cm1);
+        }
+      }
+      uint32_t As_[4] = {0u, 0u, 0u, 0u}, Bn0[4], Bn1[4];
+      if (arow) ld16(Xs + (size_t(nl) * nsb + sb) * 32 + 8 * g, As_);
+      q2_min_operand(r0w, p, Bn0);
+      const f32x4_t cn0 = mfma16(As_, Bn0, zero);
+      const float d0 = q2_d(r0w), dm0 = q2_dmin(r0w);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc0[r] = __builtin_fmaf(d0, cm0[r], __builtin_fmaf(-dm0, cn0[r], acc0[r]));
+      if constexpr (GATEUP) {
+        q2_min_operand(r1w, p, Bn1);
+        const f32x4_t cn1 = mfma16(As_, Bn1, zero);
+        const float d1 = q2_d(r1w), dm1 = q2_dmin(r1w);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc1[r] = __builtin_fmaf(d1, cm1[r], __builtin_fmaf(-dm1, cn1[r], acc1[r]));
+      }
+    }
+    // reduce the 4 waves' tiles: element (m = 4g + r, column nl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      red[(wave * 2 + 0) * 256 + (4 * g + r) * 16 + nl] = acc0[r];
+      if constexpr (GATEUP) red[(wave * 2 + 1) * 256 + (4 * g + r) * 16 + nl] = acc1[r];
+    }
+    __syncthreads();
+    {
+      const int m = tid >> 4, c = tid & 15;
+      if (m < np) {
+        float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v0 += red[(w * 2 + 0) * 256 + m * 16 + c];
+          if constexpr (GATEUP) v1 += red[(w * 2 + 1) * 256 + m * 16 + c];
+        }
+        if constexpr (GATEUP) {
+          const float hf = silu(v0) * v1;
+          const uint16_t hb = f32_to_bf16(hf);
+          const size_t o = size_t(jpair(job, t0 + m)) * a.F + r0 + c;
+          a.h[o] = hb;
+          a.h_lo[o] = f32_to_bf16(hf - bf16_to_f32(hb));
+        } else {
+          a.y[size_t(jpair(job, t0 + m)) * a.D + r0 + c] = v0;
+        }
+      }
+    }
+    (void)N;
+  }
+}
+
+template <bool GATEUP, bool XF32>
+__global__ void __launch_bounds__(256) ffn_mfma_decode_kernel(FfnArgs a, MfmaDecodeCfg cfg) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Job job;
+  const int chunks = (GATEUP ? a.F : a.D) / 16;
+  if (!pair_job(a, blockIdx.x / chunks, job)) return;
+  routed_mfma_rows<GATEUP, XF32>(a, job, blockIdx.x % chunks, cfg.np, smem);
+}
+
+static size_t mfma_decode_smem(int K, int np, int parts) {
+  const int nsb = K / 256;
+  return size_t(parts) * np * K * 2 + size_t(np) * nsb * 32 * 2 + 16 * 8 + 4 * 2 * 256 * 4;
+}
+
+// Routed experts on MFMA; the shared expert (Q8_0) on the GEMV kernels with no
+// routed jobs (u_max = 0): separate launches, so each gets its own registers.
+template <int NT, bool XF32>
+static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
+  const size_t cap = 56 * 1024;
+  FfnArgs sh = a;
+  sh.u_max = 0;
+  hipError_t err;
+  {  // gate/up
+    const int parts = XF32 ? 2 : 1;
+    const size_t per_row = size_t(parts) * a.D * 2 + size_t(a.D / 256) * 64;
+    const size_t fit = (cap - 8320) / per_row;
+    MfmaDecodeCfg c{int(std::max<size_t>(1, std::min<size_t>(size_t(std::min(a.T, 16)), fit))), parts};
+    BM_LAUNCH("ffn_mfma_gateup_kernel", (ffn_mfma_decode_kernel<true, XF32>), dim3(a.u_max * (a.F / 16)), dim3(256),
+              mfma_decode_smem(a.D, c.np, parts), stream, a, c);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.sg) {
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(a.chunks_gu), dim3(256), 0, stream, sh);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
+  {  // down
+    const size_t per_row = size_t(2) * a.F * 2 + size_t(a.F / 256) * 64;
+    const size_t fit = (cap - 8320) / per_row;
+    MfmaDecodeCfg c{int(std::max<size_t>(1, std::min<size_t>(size_t(std::min(a.T, 16)), fit))), 2};
+    BM_LAUNCH("ffn_mfma_down_kernel", (ffn_mfma_decode_kernel<false, XF32>), dim3(a.u_max * (a.D / 16)), dim3(256),
+              mfma_decode_smem(a.F, c.np, 2), stream, a, c);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.sd) {
+      BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<(NT > 2 ? 2 : NT)>), dim3(a.chunks_dn), dim3(256), 0, stream, sh);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
+  return hipSuccess;
 }
 
 // ---- combine ----------------------------------------------------------------
@@ -540,16 +766,26 @@ static hipError_t launch_decode_nt(const FfnArgs &a, bool xf32, hipStream_t stre
 }
 
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
-  // rows per block: 16 row-iterations of a wave at 64/LPR rows each
+  // rows per block: 4 row-iterations (64/LPR rows each) per wave, so every
+  // wave reuses its activation registers over several rows
   const int rpi_gu = 64 / (a.D / 64), rpi_dn = 64 / (a.F / 64);
+  const bool mfma = a.T >= 3 && a.D % 256 == 0 && a.F % 256 == 0;
   a.rows_gu = min(a.F, 16 * rpi_gu);
   a.rows_dn = min(a.D, 16 * rpi_dn);
   a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
   a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
-  a.u_max = min(a.E, a.T * a.k);
+  a.u_max = a.T * a.k;  // one job slot per pair; repeated experts exit at once
   // tokens held in registers per pass (a job's tokens beyond that take more passes)
   hipError_t err;
-  if (a.T == 1)
+  if (mfma) {
+    // routed experts on MFMA, shared expert on the GEMV rows of the same launches
+    if (a.T == 1)
+      err = xf32 ? launch_mfma_decode<1, true>(a, stream) : launch_mfma_decode<1, false>(a, stream);
+    else if (a.T == 2 || xf32)
+      err = xf32 ? launch_mfma_decode<2, true>(a, stream) : launch_mfma_decode<2, false>(a, stream);
+    else
+      err = launch_mfma_decode<NTOK, false>(a, stream);
+  } else if (a.T == 1)
     err = launch_decode_nt<1, 1>(a, xf32, stream);
   else if (a.T == 2 || xf32)
     err = launch_decode_nt<2, 2>(a, xf32, stream);

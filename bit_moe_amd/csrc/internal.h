@@ -24,6 +24,7 @@ hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void 
                           hipStream_t stream);
 hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const uint16_t *lut,
                        hipStream_t stream);
+hipError_t launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, int blocks, hipStream_t stream);
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr, const float *bias,
                         float *logits, int32_t *ids, float *wts, hipStream_t stream);
 

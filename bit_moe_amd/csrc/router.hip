@@ -119,12 +119,8 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const void *__restrict
 // (value, index) "better than": larger value, or equal value and lower index.
 BM_DEVICE bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
 
-__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int T, int E, int k,
-                                                   int32_t *__restrict__ ids, float *__restrict__ wts) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (t >= T) return;
-  const float *L = logits + int64_t(t) * E;
+// Top-k of one token's logits by one wave; lane 0 writes ids and weights.
+BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts, int lane) {
   constexpr int PER = 16;  // E <= 1024
   float v[PER];
   uint32_t taken = 0;
@@ -168,10 +164,17 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
     }
     const float inv = 1.0f / s;
     for (int j = 0; j < k; ++j) {
-      ids[int64_t(t) * k + j] = sel_i[j];
-      wts[int64_t(t) * k + j] = ex[j] * inv;
+      ids[j] = sel_i[j];
+      wts[j] = ex[j] * inv;
     }
   }
+}
+
+__global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                   int32_t *__restrict__ ids, float *__restrict__ wts) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_token(logits + int64_t(t) * E, E, k, ids + int64_t(t) * k, wts + int64_t(t) * k, threadIdx.x & 63);
 }
 
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
