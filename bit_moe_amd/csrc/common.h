@@ -51,6 +51,36 @@ BM_DEVICE float group_sum(float v) {
   return v;
 }
 
+// Wave-wide reductions on DPP: within each quad (lane ^ 1, lane ^ 2), then
+// half-row and row mirrors give every lane of a 16-lane row the row's result;
+// the four rows are combined from lanes 0, 16, 32, 48 (uniform result).
+BM_DEVICE int dpp_quad_swap1(int v) { return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false); }
+BM_DEVICE int dpp_quad_swap2(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false); }
+BM_DEVICE int dpp_half_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false); }
+BM_DEVICE int dpp_row_mirror(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); }
+
+BM_DEVICE uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(dpp_quad_swap1(int(v))));
+  v = max(v, uint32_t(dpp_quad_swap2(int(v))));
+  v = max(v, uint32_t(dpp_half_mirror(int(v))));
+  v = max(v, uint32_t(dpp_row_mirror(int(v))));
+  const uint32_t r0 = __builtin_amdgcn_readlane(int(v), 0), r1 = __builtin_amdgcn_readlane(int(v), 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(int(v), 32), r3 = __builtin_amdgcn_readlane(int(v), 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+BM_DEVICE float wave_sum(float v) {
+  v += __int_as_float(dpp_quad_swap1(__float_as_int(v)));
+  v += __int_as_float(dpp_quad_swap2(__float_as_int(v)));
+  v += __int_as_float(dpp_half_mirror(__float_as_int(v)));
+  v += __int_as_float(dpp_row_mirror(__float_as_int(v)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 BM_DEVICE float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // ---- sticky device status record (int64 code flags, int64 detail) --------

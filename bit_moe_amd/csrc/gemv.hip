@@ -305,8 +305,7 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
   }
   const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
   using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
-  // raw bytes of the lane's unit in row iteration `it` (software-pipelined one
-  // iteration ahead so the next rows' loads overlap this row's arithmetic)
+  // raw bytes of the lane's unit in row iteration `it`
   auto load_it = [&](int it, Raw &rg, Raw &ru) {
     const int r = min(r_begin + it * RPI + rsub, r_end - 1);
     const int unit = r * LPR + jj;
@@ -320,67 +319,77 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
     }
   };
   const int n_it = (r_end - r_begin + RPI - 1) / RPI;
-  Raw cg, cu;
-  if (wave < n_it) load_it(wave, cg, cu);
-  for (int it = wave; it < n_it; it += 4) {
-    Raw ng, nu;
-    if (it + 4 < n_it) load_it(it + 4, ng, nu);
-    const int r = r_begin + it * RPI + rsub;
-    const bool active = r < r_end;
-    float g[NV], u[NV];
+  // the wave's row iterations it = wave, wave + 4, ...: the weight loads of up
+  // to DEPTH of them are issued before any arithmetic, so their memory
+  // latencies overlap
+  constexpr int DEPTH = IS_Q8 ? 1 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));
+  for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
+    Raw rg[DEPTH], ru[DEPTH];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) g[v] = u[v] = 0.f;
-    if constexpr (IS_Q8) {
-      q8_unit_dot<NV>(cg, X, g);
-      q8_unit_dot<NV>(cu, X, u);
-    } else {
-      const int unit = (active ? r : r_end - 1) * LPR + jj;
-      q2_unit_dot<NV>(cg, unit & 1, X, g);
-      q2_unit_dot<NV>(cu, unit & 1, X, u);
-    }
+    for (int d = 0; d < DEPTH; ++d)
+      if (it0 + 4 * d < n_it) load_it(it0 + 4 * d, rg[d], ru[d]);
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      float gs, us;
-      if constexpr (XF32) {
-        gs = g[2 * i] + g[2 * i + 1];
-        us = u[2 * i] + u[2 * i + 1];
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = it0 + 4 * d;
+      if (it >= n_it) break;
+      const int r = r_begin + it * RPI + rsub;
+      const bool active = r < r_end;
+      float g[NV], u[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) g[v] = u[v] = 0.f;
+      if constexpr (IS_Q8) {
+        q8_unit_dot<NV>(rg[d], X, g);
+        q8_unit_dot<NV>(ru[d], X, u);
       } else {
-        gs = g[i];
-        us = u[i];
+        const int unit = (active ? r : r_end - 1) * LPR + jj;
+        q2_unit_dot<NV>(rg[d], unit & 1, X, g);
+        q2_unit_dot<NV>(ru[d], unit & 1, X, u);
       }
-      for (int o = LPR / 2; o > 0; o >>= 1) {  // sum over the LPR lanes of the row
-        gs += __shfl_xor(gs, o);
-        us += __shfl_xor(us, o);
-      }
-      if (active && jj == 0 && i < nt) {
-        const float hf = silu(gs) * us;
-        const uint16_t hv = f32_to_bf16(hf);
-        const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + i)) * a.F + r : size_t(jpair(job, t0 + i)) * a.F + r;
-        // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
-        // rounding of h would dominate the layer's output error
-        (IS_Q8 ? a.hs : a.h)[o] = hv;
-        (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float gs, us;
+        if constexpr (XF32) {
+          gs = g[2 * i] + g[2 * i + 1];
+          us = u[2 * i] + u[2 * i + 1];
+        } else {
+          gs = g[i];
+          us = u[i];
+        }
+        for (int o = LPR / 2; o > 0; o >>= 1) {  // sum over the LPR lanes of the row
+          gs += __shfl_xor(gs, o);
+          us += __shfl_xor(us, o);
+        }
+        if (active && jj == 0 && i < nt) {
+          const float hf = silu(gs) * us;
+          const uint16_t hv = f32_to_bf16(hf);
+          const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + i)) * a.F + r : size_t(jpair(job, t0 + i)) * a.F + r;
+          // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
+          // rounding of h would dominate the layer's output error
+          (IS_Q8 ? a.hs : a.h)[o] = hv;
+          (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
+        }
       }
     }
-    cg = ng;
-    cu = nu;
   }
 }
 
+// Grid: the shared expert's row chunks first (its Q8_0 rows are the heaviest,
+// so they start first), then u_max routed job slots x chunks_gu row chunks.
 template <int NT, bool XF32>
 __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
   Job job;
-  const int n_routed_blocks = a.u_max * a.chunks_gu;
-  const bool shared = int(blockIdx.x) >= n_routed_blocks;
-  int chunk;
-  if (!shared) {
-    if (!pair_job(a, blockIdx.x / a.chunks_gu, job)) return;
-    chunk = blockIdx.x % a.chunks_gu;
-  } else {
+  int r_begin, r_end;
+  const bool shared = int(blockIdx.x) < a.chunks_sg;
+  if (shared) {
     shared_job(a, job);
-    chunk = blockIdx.x - n_routed_blocks;
+    r_begin = blockIdx.x * a.rows_sg;
+    r_end = min(a.F, r_begin + a.rows_sg);
+  } else {
+    const int b = blockIdx.x - a.chunks_sg;
+    if (!pair_job(a, b / a.chunks_gu, job)) return;
+    r_begin = (b % a.chunks_gu) * a.rows_gu;
+    r_end = min(a.F, r_begin + a.rows_gu);
   }
-  const int r_begin = chunk * a.rows_gu, r_end = min(a.F, r_begin + a.rows_gu);
   for (int t0 = 0; t0 < job.n; t0 += NT) {
     const int nt = min(NT, job.n - t0);
     if (shared)
@@ -427,51 +436,57 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
     }
   };
   const int n_it = (r_end - r_begin + RPI - 1) / RPI;
-  Raw cw;
-  if (wave < n_it) load_it(wave, cw);
-  for (int it = wave; it < n_it; it += 4) {
-    Raw nw;
-    if (it + 4 < n_it) load_it(it + 4, nw);
-    const int r = r_begin + it * RPI + rsub;
-    const bool active = r < r_end;
-    float y[NV];
+  constexpr int DEPTH = IS_Q8 ? 1 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));  // as in gate/up
+  for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
+    Raw rw[DEPTH];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) y[v] = 0.f;
-    if constexpr (IS_Q8) {
-      q8_unit_dot<NV>(cw, X, y);
-    } else {
-      const int unit = (active ? r : r_end - 1) * LPR + jj;
-      q2_unit_dot<NV>(cw, unit & 1, X, y);
-    }
+    for (int d = 0; d < DEPTH; ++d)
+      if (it0 + 4 * d < n_it) load_it(it0 + 4 * d, rw[d]);
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      float ys = XF32 ? y[2 * i] + y[2 * i + 1] : y[i];
-      for (int o = LPR / 2; o > 0; o >>= 1) ys += __shfl_xor(ys, o);
-      if (active && jj == 0 && i < nt) {
-        if constexpr (IS_Q8)
-          a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = ys;
-        else
-          a.y[size_t(jpair(job, t0 + i)) * a.D + r] = ys;
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = it0 + 4 * d;
+      if (it >= n_it) break;
+      const int r = r_begin + it * RPI + rsub;
+      const bool active = r < r_end;
+      float y[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) y[v] = 0.f;
+      if constexpr (IS_Q8) {
+        q8_unit_dot<NV>(rw[d], X, y);
+      } else {
+        const int unit = (active ? r : r_end - 1) * LPR + jj;
+        q2_unit_dot<NV>(rw[d], unit & 1, X, y);
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float ys = XF32 ? y[2 * i] + y[2 * i + 1] : y[i];
+        for (int o = LPR / 2; o > 0; o >>= 1) ys += __shfl_xor(ys, o);
+        if (active && jj == 0 && i < nt) {
+          if constexpr (IS_Q8)
+            a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = ys;
+          else
+            a.y[size_t(jpair(job, t0 + i)) * a.D + r] = ys;
+        }
       }
     }
-    cw = nw;
   }
 }
 
 template <int NT>
 __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
   Job job;
-  const int n_routed_blocks = a.u_max * a.chunks_dn;
-  const bool shared = int(blockIdx.x) >= n_routed_blocks;
-  int chunk;
-  if (!shared) {
-    if (!pair_job(a, blockIdx.x / a.chunks_dn, job)) return;
-    chunk = blockIdx.x % a.chunks_dn;
-  } else {
+  int r_begin, r_end;
+  const bool shared = int(blockIdx.x) < a.chunks_sd;
+  if (shared) {
     shared_job(a, job);
-    chunk = blockIdx.x - n_routed_blocks;
+    r_begin = blockIdx.x * a.rows_sd;
+    r_end = min(a.D, r_begin + a.rows_sd);
+  } else {
+    const int b = blockIdx.x - a.chunks_sd;
+    if (!pair_job(a, b / a.chunks_dn, job)) return;
+    r_begin = (b % a.chunks_dn) * a.rows_dn;
+    r_end = min(a.D, r_begin + a.rows_dn);
   }
-  const int r_begin = chunk * a.rows_dn, r_end = min(a.D, r_begin + a.rows_dn);
   for (int t0 = 0; t0 < job.n; t0 += NT) {
     const int nt = min(NT, job.n - t0);
     if (shared)
@@ -677,7 +692,7 @@ template <int NT, bool XF32>
 static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
   const size_t cap = 56 * 1024;
   FfnArgs sh = a;
-  sh.u_max = 0;
+  sh.u_max = 0;  // shared row chunks only
   hipError_t err;
   {  // gate/up
     const int parts = XF32 ? 2 : 1;
@@ -688,7 +703,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
               mfma_decode_smem(a.D, c.np, parts), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.sg) {
-      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(a.chunks_gu), dim3(256), 0, stream, sh);
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(a.chunks_sg), dim3(256), 0, stream, sh);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
@@ -700,7 +715,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
               mfma_decode_smem(a.F, c.np, 2), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (a.sd) {
-      BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<(NT > 2 ? 2 : NT)>), dim3(a.chunks_dn), dim3(256), 0, stream, sh);
+      BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<(NT > 2 ? 2 : NT)>), dim3(a.chunks_sd), dim3(256), 0, stream, sh);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
@@ -752,9 +767,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 
 template <int NT_GU, int NT_DN>
 static hipError_t launch_decode_nt(const FfnArgs &a, bool xf32, hipStream_t stream) {
-  const int shared_gu = a.sg ? a.chunks_gu : 0;
-  const int shared_dn = a.sd ? a.chunks_dn : 0;
-  dim3 g1(a.u_max * a.chunks_gu + shared_gu), g2(a.u_max * a.chunks_dn + shared_dn);
+  dim3 g1(a.chunks_sg + a.u_max * a.chunks_gu), g2(a.chunks_sd + a.u_max * a.chunks_dn);
   if (xf32)
     BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_GU, true>), g1, dim3(256), 0, stream, a);
   else
@@ -774,6 +787,12 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
   a.rows_dn = min(a.D, 16 * rpi_dn);
   a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
   a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
+  // shared expert: one row iteration per wave, since a Q8_0 row is 3.2x the
+  // bytes of a 2-bit row; its blocks then carry about as many bytes as a routed one
+  a.rows_sg = min(a.F, 4 * rpi_gu);
+  a.rows_sd = min(a.D, 4 * rpi_dn);
+  a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
+  a.chunks_sd = a.sd ? (a.D + a.rows_sd - 1) / a.rows_sd : 0;
   a.u_max = a.T * a.k;  // one job slot per pair; repeated experts exit at once
   // tokens held in registers per pass (a job's tokens beyond that take more passes)
   hipError_t err;

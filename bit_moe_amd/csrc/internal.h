@@ -57,8 +57,10 @@ struct FfnArgs {
   void *out;
   int out_bf16;
   int64_t *status;
-  int chunks_gu, rows_gu;
-  int chunks_dn, rows_dn;
+  int chunks_gu, rows_gu;   // routed gate/up: row chunks per job, rows per chunk
+  int chunks_dn, rows_dn;   // routed down
+  int chunks_sg, rows_sg;   // shared gate/up (0 chunks: no shared blocks in the launch)
+  int chunks_sd, rows_sd;   // shared down
   int u_max;
 };
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream);

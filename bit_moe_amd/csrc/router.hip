@@ -7,15 +7,16 @@
 // selected experts, which equals the full softmax renormalised over them.
 //
 // Kernels
-//  router_gemv_kernel   T <= 8: one wave per expert row; every lane streams
-//                       16-byte slices of the row (coalesced 1 KB per wave
-//                       load) and keeps one partial sum per token.  HBM-bound
-//                       on the 4 B/weight router matrix.
+//  router_gemv_kernel   T <= 8: one block per expert row; every thread loads
+//                       its 16-byte slices of the row at once and keeps one
+//                       partial sum per token.  HBM-bound on the 4 B/weight
+//                       router matrix.
 //  router_tile_kernel   T > 8: 64 tokens x 64 experts per 256-thread block,
 //                       K staged through LDS in steps of 32, 4x4 outputs per
 //                       thread.
 //  topk_kernel          one wave per token: k rounds of a wave-wide
-//                       (value, index) argmax over the E logits.
+//                       maximum over order-preserving integer keys of the
+//                       logits (DPP), ties resolved by ballot.
 #include "common.h"
 #include "internal.h"
 
@@ -31,38 +32,47 @@ BM_DEVICE float4 load_x4(const void *x, int64_t idx) {
   }
 }
 
+// One block per expert row: thread i reads the float4 slices 4i + 1024j of the
+// row (all of them issued before the arithmetic), the block sums through LDS.
 template <bool XBF16>
 __global__ void __launch_bounds__(256) router_gemv_kernel(const void *__restrict__ x, int T, int D, int E,
                                                           const float *__restrict__ wr,
                                                           const float *__restrict__ bias,
                                                           float *__restrict__ logits) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (e >= E) return;
-  float acc[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = 0.f;
+  constexpr int MAXJ = 4;  // D <= 4096
+  __shared__ float part[4][8];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *row = wr + int64_t(e) * D;
-  for (int c = lane * 4; c < D; c += 256) {
-    const float4 w = *reinterpret_cast<const float4 *>(row + c);
+  float4 w[MAXJ];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t < T) {
-        const float4 v = load_x4<XBF16>(x, int64_t(t) * D + c);
-        acc[t] = __builtin_fmaf(w.x, v.x, acc[t]);
-        acc[t] = __builtin_fmaf(w.y, v.y, acc[t]);
-        acc[t] = __builtin_fmaf(w.z, v.z, acc[t]);
-        acc[t] = __builtin_fmaf(w.w, v.w, acc[t]);
-      }
-    }
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = 4 * tid + 1024 * j;
+    w[j] = c < D ? *reinterpret_cast<const float4 *>(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  const float b = bias ? bias[e] : 0.f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if (t < T) {
-      const float s = group_sum<64>(acc[t]);
-      if (lane == 0) logits[int64_t(t) * E + e] = s + b;
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXJ; ++j) {
+        const int c = 4 * tid + 1024 * j;
+        if (c < D) {
+          const float4 v = load_x4<XBF16>(x, int64_t(t) * D + c);
+          acc = __builtin_fmaf(w[j].x, v.x, acc);
+          acc = __builtin_fmaf(w[j].y, v.y, acc);
+          acc = __builtin_fmaf(w[j].z, v.z, acc);
+          acc = __builtin_fmaf(w[j].w, v.w, acc);
+        }
+      }
+      const float s = wave_sum(acc);
+      if (lane == 0) part[wave][t] = s;
     }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const float s = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+    logits[int64_t(tid) * E + e] = s + (bias ? bias[e] : 0.f);
   }
 }
 
@@ -116,44 +126,50 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const void *__restrict
   }
 }
 
-// (value, index) "better than": larger value, or equal value and lower index.
-BM_DEVICE bool better(float v, int i, float v2, int i2) { return v > v2 || (v == v2 && i < i2); }
+// Order-preserving key of a float32 logit: larger value -> larger key, +0 and
+// -0 alike; NaN and absent entries get key 0, below every number.
+BM_DEVICE uint32_t logit_key(float v) {
+  if (v != v) return 0u;
+  const uint32_t u = __float_as_uint(v + 0.0f);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+BM_DEVICE float key_logit(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 // Top-k of one token's logits by one wave; lane 0 writes ids and weights.
+// Round j: the wave-wide largest key M (DPP reduction); the selected expert is
+// the lowest index holding M (lowest slot i, then lowest lane, by ballot), so
+// an exact tie goes to the lower expert index.
 BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts, int lane) {
   constexpr int PER = 16;  // E <= 1024
-  float v[PER];
-  uint32_t taken = 0;
+  uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? L[e] : -INFINITY;
+    key[i] = e < E ? logit_key(L[e]) : 0u;
   }
   float sel_v[8];
   int sel_i[8];
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && better(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
+    for (int i = 0; i < PER; ++i) m = max(m, key[i]);
+    const uint32_t M = wave_max_u32(m);
+    int bi = -1;  // only NaN logits left: no valid expert
+    if (M != 0u) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const uint64_t hit = __ballot(key[i] == M);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          bi = l + 64 * i;
+          if (lane == l) key[i] = 0u;
+          break;
+        }
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi == 0x7FFFFFFF) bi = -1;  // only NaN logits left: no valid expert
-    else if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    sel_v[j] = bv;
+    sel_v[j] = bi < 0 ? -INFINITY : key_logit(M);
     sel_i[j] = bi;
   }
   if (lane == 0) {
@@ -180,7 +196,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
                         const float *bias, float *logits, int32_t *ids, float *wts, hipStream_t stream) {
   if (T <= 8) {
-    dim3 grid((E + 3) / 4);
+    dim3 grid(E);
     if (xbf16)
       BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
     else

@@ -158,6 +158,42 @@ def test_router_prefill_zipf_bias():
     assert exact + ties == 4096 and exact > 4000
 
 
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_router_exact_ties_and_nan_row(T):
+    """Experts 3g, 3g+1, 3g+2 share one router row, so their logits are equal
+    bit for bit on the device as in the oracle: a selected expert's lower
+    group mates must be selected before it.  Expert 5's row is NaN: never
+    selected (the oracle sees it as -inf)."""
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 3)
+    cfg = ld.cfg
+    E, k = cfg.n_experts, cfg.top_k
+    base = ld.router()
+    wr = base[np.arange(E) // 3].copy()
+    wr[5] = np.nan
+    layer = device_layer(ld, host_bytes=False)
+    layer.w_router = torch.from_numpy(wr).cuda()
+    x = x_device(ld, 7, T)
+    ws = bm.workspace(layer, T)
+    ids, w = bm.route(layer, x, ws)
+    ids, w = ids.cpu().numpy(), w.cpu().numpy()
+    assert not np.any(ids == 5)
+    wr_ref = wr.copy()
+    wr_ref[5] = 0.0
+    L = moe.router_logits(ld.x_values(7, T), wr_ref)
+    L[:, 5] = -np.inf
+    r_ids = moe.topk_ids(L, k)
+    exact, ties, bad = compare.compare_ids(ids, r_ids, L)
+    assert not bad and exact + ties == T
+    for t in range(T):
+        pos = {int(e): j for j, e in enumerate(ids[t])}
+        for e, j in pos.items():
+            for e2 in range(3 * (e // 3), e):
+                if e2 == 5:
+                    continue
+                assert e2 in pos and pos[e2] < j, (t, ids[t])
+    assert np.allclose(w, moe.weights_for_selection(L, ids), rtol=2e-5, atol=1e-7)
+
+
 # ------------------------------------------------------------------ plan
 
 
