@@ -69,6 +69,36 @@ BM_DEVICE uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// Sum over aligned groups of `lpr` lanes (lpr = 1, 2, 4, ..., 64), the result
+// in every lane of the group: DPP within rows of 16 lanes, then the gfx950
+// row swaps (v_permlane16_swap, v_permlane32_swap).  Each step adds the same
+// two operands in the same order in both partner lanes, so all lanes agree.
+BM_DEVICE float swap_add16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+BM_DEVICE float swap_add32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+BM_DEVICE float lane_group_sum(float v, int lpr) {
+  if (lpr >= 2) v += __int_as_float(dpp_quad_swap1(__float_as_int(v)));
+  if (lpr >= 4) v += __int_as_float(dpp_quad_swap2(__float_as_int(v)));
+  if (lpr >= 8) v += __int_as_float(dpp_half_mirror(__float_as_int(v)));
+  if (lpr >= 16) v += __int_as_float(dpp_row_mirror(__float_as_int(v)));
+  if (lpr >= 32) v = swap_add16(v);
+  if (lpr >= 64) v = swap_add32(v);
+  return v;
+}
+
+// (a & mask) | c in one v_and_or_b32 (the compiler splits it in two when both
+// constants are literals); mask comes from an SGPR, c from a VGPR
+BM_DEVICE uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+}
+
 BM_DEVICE float wave_sum(float v) {
   v += __int_as_float(dpp_quad_swap1(__float_as_int(v)));
   v += __int_as_float(dpp_quad_swap2(__float_as_int(v)));

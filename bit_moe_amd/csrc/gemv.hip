@@ -54,6 +54,9 @@ struct XQ2 {  // one bf16 "virtual token" for one Q2 unit
   float sum[4], c[4];
 };
 
+constexpr uint32_t BF16_128x2 = 0x43004300u;  // two bf16 128.0
+constexpr uint32_t BF16_ONEx2 = 0x3F803F80u;  // two bf16 1.0
+
 BM_DEVICE float inv_f(int s) { return s == 0 ? 1.f : (s == 1 ? 0.25f : 0.0625f); }
 
 BM_DEVICE void xq2_finish(XQ2 &X) {
@@ -68,7 +71,7 @@ BM_DEVICE void xq2_from_words(XQ2 &X, int s, const uint32_t (&d)[8]) {
     const uint32_t lo = d[2 * j], hi = d[2 * j + 1];
     X.a[4 * s + j] = (lo & 0xFFFFu) | (hi << 16);
     X.b[4 * s + j] = (lo >> 16) | (hi & 0xFFFF0000u);
-    sum += (bf16_lo(lo) + bf16_hi(lo)) + (bf16_lo(hi) + bf16_hi(hi));
+    sum = dot2_bf16(hi, BF16_ONEx2, dot2_bf16(lo, BF16_ONEx2, sum));
   }
   X.sum[s] = sum;
 }
@@ -131,7 +134,7 @@ BM_DEVICE void load_xq8_bf16(const uint16_t *row, int c0, XQ8 &X) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         X.p[16 * b + 4 * q + i] = d[i];
-        sum += bf16_lo(d[i]) + bf16_hi(d[i]);
+        sum = dot2_bf16(d[i], BF16_ONEx2, sum);
       }
     }
     X.c[b] = -128.f * sum;
@@ -202,11 +205,11 @@ BM_DEVICE void q2_unit_dot(const Q2Unit &u, int p, const XQ2 *X, float *out) {
       uint32_t A, B;
       if (s < 3) {
         const uint32_t m = 0x00030003u << (2 * s);
-        A = (w[j] & m) | 0x43004300u;
-        B = ((w[j] >> 8) & m) | 0x43004300u;
+        A = and_or(w[j], m, BF16_128x2);
+        B = and_or(w[j] >> 8, m, BF16_128x2);
       } else {
-        A = ((w[j] >> 2) & 0x00300030u) | 0x43004300u;
-        B = ((w[j] >> 10) & 0x00300030u) | 0x43004300u;
+        A = and_or(w[j] >> 2, 0x00300030u, BF16_128x2);
+        B = and_or(w[j] >> 10, 0x00300030u, BF16_128x2);
       }
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
@@ -355,10 +358,8 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
           gs = g[i];
           us = u[i];
         }
-        for (int o = LPR / 2; o > 0; o >>= 1) {  // sum over the LPR lanes of the row
-          gs += __shfl_xor(gs, o);
-          us += __shfl_xor(us, o);
-        }
+        gs = lane_group_sum(gs, LPR);  // sum over the LPR lanes of the row
+        us = lane_group_sum(us, LPR);
         if (active && jj == 0 && i < nt) {
           const float hf = silu(gs) * us;
           const uint16_t hv = f32_to_bf16(hf);
@@ -460,7 +461,7 @@ BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r
 #pragma unroll
       for (int i = 0; i < NT; ++i) {
         float ys = XF32 ? y[2 * i] + y[2 * i + 1] : y[i];
-        for (int o = LPR / 2; o > 0; o >>= 1) ys += __shfl_xor(ys, o);
+        ys = lane_group_sum(ys, LPR);
         if (active && jj == 0 && i < nt) {
           if constexpr (IS_Q8)
             a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = ys;
