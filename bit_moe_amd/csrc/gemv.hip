@@ -45,456 +45,457 @@ typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef u32x2 __attribute__((aligned(4))) u32x2_a4;
 
-constexpr int NTOK = 4;  // tokens held in registers per pass
+constexpr int NTOK = 4;  // tokens per pass of a job
 
-// ---- activation operands ----------------------------------------------------
-
-struct XQ2 {  // one bf16 "virtual token" for one Q2 unit
-  uint32_t a[16], b[16];
-  float sum[4], c[4];
-};
+// ---- GEMV: weights and activation operands staged in LDS ---------------------
+// A block owns one job (a routed expert of the union, or the shared expert)
+// and a chunk of consecutive weight rows.  Its 256 threads copy the chunk's
+// bytes (contiguous in HBM) into LDS with 16-byte direct-to-LDS loads, fully
+// coalesced, while they build the activation operands of the job's tokens in
+// LDS once for the whole block.  Each wave then computes rows from LDS: lane
+// jj = lane % LPR owns unit jj (64 weights) of every row it visits, LPR lanes
+// per row, RPI = 64 / LPR rows per wave iteration.
 
 constexpr uint32_t BF16_128x2 = 0x43004300u;  // two bf16 128.0
 constexpr uint32_t BF16_ONEx2 = 0x3F803F80u;  // two bf16 1.0
 
 BM_DEVICE float inv_f(int s) { return s == 0 ? 1.f : (s == 1 ? 0.25f : 0.0625f); }
 
-BM_DEVICE void xq2_finish(XQ2 &X) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) X.c[s] = -128.f * inv_f(s) * X.sum[s];
-}
-
-BM_DEVICE void xq2_from_words(XQ2 &X, int s, const uint32_t (&d)[8]) {
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = d[2 * j], hi = d[2 * j + 1];
-    X.a[4 * s + j] = (lo & 0xFFFFu) | (hi << 16);
-    X.b[4 * s + j] = (lo >> 16) | (hi & 0xFFFF0000u);
-    sum = dot2_bf16(hi, BF16_ONEx2, dot2_bf16(lo, BF16_ONEx2, sum));
-  }
-  X.sum[s] = sum;
-}
-
-// bf16 activations: 16 contiguous values at row + c0 + 32 s
-BM_DEVICE void load_xq2_bf16(const uint16_t *row, int c0, XQ2 &X) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(row + c0 + 32 * s);
-    const uint4 v0 = p[0], v1 = p[1];
-    const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    xq2_from_words(X, s, d);
-  }
-  xq2_finish(X);
-}
-
-// float32 activations: split exactly enough into bf16 hi + bf16 lo parts
-// (x - hi is exact in float32), two virtual tokens whose results are summed.
-BM_DEVICE void load_xq2_f32(const float *row, int c0, XQ2 &Xh, XQ2 &Xl) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const float4 *p = reinterpret_cast<const float4 *>(row + c0 + 32 * s);
-    uint32_t dh[8], dl[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 v = p[q];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      uint32_t hb[4], lb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = f32_to_bf16(f[i]);
-        lb[i] = f32_to_bf16(f[i] - bf16_to_f32(uint16_t(hb[i])));
-      }
-      dh[2 * q] = hb[0] | (hb[1] << 16);
-      dh[2 * q + 1] = hb[2] | (hb[3] << 16);
-      dl[2 * q] = lb[0] | (lb[1] << 16);
-      dl[2 * q + 1] = lb[2] | (lb[3] << 16);
-    }
-    xq2_from_words(Xh, s, dh);
-    xq2_from_words(Xl, s, dl);
-  }
-  xq2_finish(Xh);
-  xq2_finish(Xl);
-}
-
-struct XQ8 {  // one bf16 virtual token for one Q8_0 unit (two 32-weight blocks)
-  uint32_t p[32];
-  float c[2];
-};
-
-BM_DEVICE void load_xq8_bf16(const uint16_t *row, int c0, XQ8 &X) {
-  const uint4 *p = reinterpret_cast<const uint4 *>(row + c0);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = p[4 * b + q];
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        X.p[16 * b + 4 * q + i] = d[i];
-        sum = dot2_bf16(d[i], BF16_ONEx2, sum);
-      }
-    }
-    X.c[b] = -128.f * sum;
-  }
-}
-
-BM_DEVICE void load_xq8_f32(const float *row, int c0, XQ8 &Xh, XQ8 &Xl) {
-  const float4 *p = reinterpret_cast<const float4 *>(row + c0);
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float sh = 0.f, sl = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const float4 v = p[8 * b + q];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-      uint32_t hb[4], lb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = f32_to_bf16(f[i]);
-        const float hf = bf16_to_f32(uint16_t(hb[i]));
-        lb[i] = f32_to_bf16(f[i] - hf);
-        sh += hf;
-        sl += bf16_to_f32(uint16_t(lb[i]));
-      }
-      Xh.p[16 * b + 2 * q] = hb[0] | (hb[1] << 16);
-      Xh.p[16 * b + 2 * q + 1] = hb[2] | (hb[3] << 16);
-      Xl.p[16 * b + 2 * q] = lb[0] | (lb[1] << 16);
-      Xl.p[16 * b + 2 * q + 1] = lb[2] | (lb[3] << 16);
-    }
-    Xh.c[b] = -128.f * sh;
-    Xl.c[b] = -128.f * sl;
-  }
-}
-
-// ---- one row unit against NV virtual tokens ----------------------------------
-
-struct Q2Unit {  // raw bytes of one lane's quarter super-block
-  u32x4 q;
-  u32x2 sc;
-  uint32_t dd;
-};
-
-BM_DEVICE Q2Unit q2_unit_load(const uint8_t *sb, int h, int p) {
-  Q2Unit r;
-  r.q = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * h + 16 * p);
-  r.sc = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * h);
-  r.dd = *reinterpret_cast<const uint32_t *>(sb + 80);
-  return r;
-}
-
-template <int NV>
-BM_DEVICE void q2_unit_dot(const Q2Unit &u, int p, const XQ2 *X, float *out) {
-  const float d = half_to_f32(u.dd & 0xFFFFu), dmin = half_to_f32(u.dd >> 16);
-  const uint32_t w[4] = {u.q.x, u.q.y, u.q.z, u.q.w};
-  const uint32_t sw0 = u.sc.x >> (8 * p), sw1 = u.sc.y >> (8 * p);
-  float yd[NV], ym[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) yd[v] = ym[v] = 0.f;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t sbyte = ((s < 2 ? sw0 : sw1) >> (16 * (s & 1))) & 0xFFu;
-    const float scf = float(sbyte & 15u), mf = float(sbyte >> 4);
-    float acc[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t A, B;
-      if (s < 3) {
-        const uint32_t m = 0x00030003u << (2 * s);
-        A = and_or(w[j], m, BF16_128x2);
-        B = and_or(w[j] >> 8, m, BF16_128x2);
-      } else {
-        A = and_or(w[j] >> 2, 0x00300030u, BF16_128x2);
-        B = and_or(w[j] >> 10, 0x00300030u, BF16_128x2);
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        acc[v] = dot2_bf16(A, X[v].a[4 * s + j], acc[v]);
-        acc[v] = dot2_bf16(B, X[v].b[4 * s + j], acc[v]);
-      }
-    }
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const float qx = __builtin_fmaf(acc[v], inv_f(s), X[v].c[s]);
-      yd[v] = __builtin_fmaf(scf, qx, yd[v]);
-      ym[v] = __builtin_fmaf(mf, X[v].sum[s], ym[v]);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) out[v] += d * yd[v] - dmin * ym[v];
-}
-
-struct Q8Unit {  // raw bytes of one lane's two Q8_0 blocks (68 bytes)
-  uint32_t dw[17];
-};
-
-BM_DEVICE Q8Unit q8_unit_load(const uint8_t *u68) {
-  Q8Unit r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4 v = *reinterpret_cast<const u32x4_a4 *>(u68 + 16 * i);
-    r.dw[4 * i] = v.x;
-    r.dw[4 * i + 1] = v.y;
-    r.dw[4 * i + 2] = v.z;
-    r.dw[4 * i + 3] = v.w;
-  }
-  r.dw[16] = *reinterpret_cast<const uint32_t *>(u68 + 64);
-  return r;
-}
-
-template <int NV>
-BM_DEVICE void q8_unit_dot(const Q8Unit &u, const XQ8 *X, float *out) {
-  const float dA = half_to_f32(u.dw[0] & 0xFFFFu), dB = half_to_f32(u.dw[8] >> 16);
-  uint32_t ux[17];
-#pragma unroll
-  for (int i = 0; i < 17; ++i) ux[i] = u.dw[i] ^ 0x80808080u;  // q + 128 as unsigned bytes
-  float acc[2][NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) acc[0][v] = acc[1][v] = 0.f;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int i = 0; i < 32; i += 2) {
-      const int byte0 = (b ? 36 : 2) + i;  // byte offset of q_i inside the 68-byte unit
-      const int byte1 = byte0 + 1;
-      const float f0 = float((ux[byte0 >> 2] >> (8 * (byte0 & 3))) & 0xFFu);
-      const float f1 = float((ux[byte1 >> 2] >> (8 * (byte1 & 3))) & 0xFFu);
-      const uint32_t pr = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) acc[b][v] = dot2_bf16(pr, X[v].p[16 * b + i / 2], acc[b][v]);
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) out[v] += dA * (acc[0][v] + X[v].c[0]) + dB * (acc[1][v] + X[v].c[1]);
-}
-
-// ---- job bookkeeping -------------------------------------------------------
-
-
-
+// first column of Q2 unit (super-block n of the row, quarter q)
 BM_DEVICE int q2_c0(int n, int q, int K) { return (256 * n + 128 * (q >> 1) + 16 * (q & 1)) % K; }
 
-// ---- gate/up ----------------------------------------------------------------
+// Activation operands in LDS, groups of four dwords XL[(t * XG + g) * LPR + jj]
+// for token t of the pass and lane slot jj; PARTS bf16 parts add up to the
+// activations (1: bf16 x; 2: hi + lo of float32 x or of h) and multiply the
+// same weight operand into the same accumulator.
+//   Q2 unit: g = 8 part + s      a[part][4s .. 4s+3]  pairs of code bytes 0, 2
+//            g = 8 part + 4 + s  b[part][4s .. 4s+3]  pairs of code bytes 1, 3
+//            g = 8 PARTS         X_0 .. X_3 (sub-block sums over all parts)
+//            g = 8 PARTS + 1     c_s = -128 X_s / F_s,  F_s = 1, 4, 16, 16
+//   Q8_0 unit (two blocks): g = 8 part + i  pairs 4i .. 4i+3 in order;
+//            g = 8 PARTS: (-128 * block-0 sum, -128 * block-1 sum)
+template <int PARTS>
+constexpr int xgroups() { return 8 * PARTS + 2; }
 
-// Rows [r_begin, r_end) of one job for tokens t0 .. t0+nt-1 of the job.
-// IS_Q8: shared expert (Q8_0) instead of a routed expert (Q2).
-template <int NT, bool XF32, bool IS_Q8>
-BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r_begin, int r_end) {
-  constexpr int NV = XF32 ? 2 * NT : NT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = a.D, LPR = K / 64, RPI = 64 / LPR;
-  const int jj = lane % LPR, rsub = lane / LPR;
-  // the lane's columns do not depend on the row: K is a multiple of 128
-  const int c0 = IS_Q8 ? jj * 64 : q2_c0(jj >> 2, jj & 3, K);
-  typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
+// 8 floats at p -> bf16 hi words and lo words (lo = v - hi, exact)
+BM_DEVICE void split8(const float *p, uint32_t *dh, uint32_t *dl) {
+  const float4 v0 = reinterpret_cast<const float4 *>(p)[0], v1 = reinterpret_cast<const float4 *>(p)[1];
+  const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int t = jtok(a, job, t0 + min(i, nt - 1));
-    if constexpr (IS_Q8) {
-      if constexpr (XF32)
-        load_xq8_f32(static_cast<const float *>(a.x) + size_t(t) * K, c0, X[2 * i], X[2 * i + 1]);
-      else
-        load_xq8_bf16(static_cast<const uint16_t *>(a.x) + size_t(t) * K, c0, X[i]);
-    } else {
-      if constexpr (XF32)
-        load_xq2_f32(static_cast<const float *>(a.x) + size_t(t) * K, c0, X[2 * i], X[2 * i + 1]);
-      else
-        load_xq2_bf16(static_cast<const uint16_t *>(a.x) + size_t(t) * K, c0, X[i]);
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t h0 = f32_to_bf16(f[2 * q]), h1 = f32_to_bf16(f[2 * q + 1]);
+    dh[q] = h0 | (h1 << 16);
+    dl[q] = f32_to_bf16(f[2 * q] - bf16_to_f32(uint16_t(h0))) |
+            (uint32_t(f32_to_bf16(f[2 * q + 1] - bf16_to_f32(uint16_t(h1)))) << 16);
+  }
+}
+
+// n consecutive activations (n = 16 or 32) of part `part` as bf16 words: from
+// a float32 row (split) or from bf16 rows hi / lo
+template <bool SRC_F32>
+BM_DEVICE void act_words(const void *hi, const void *lo, size_t off, int part, int n, uint32_t *d) {
+  if constexpr (SRC_F32) {
+    const float *p = static_cast<const float *>(hi) + off;
+    uint32_t th[4], tl[4];
+    for (int i = 0; i < n / 8; ++i) {
+      split8(p + 8 * i, th, tl);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) d[4 * i + w] = part ? tl[w] : th[w];
+    }
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(part ? lo : hi) + off);
+    for (int i = 0; i < n / 8; ++i) {
+      const uint4 v = p[i];
+      d[4 * i] = v.x;
+      d[4 * i + 1] = v.y;
+      d[4 * i + 2] = v.z;
+      d[4 * i + 3] = v.w;
     }
   }
-  const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
-  using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
-  // raw bytes of the lane's unit in row iteration `it`
-  auto load_it = [&](int it, Raw &rg, Raw &ru) {
-    const int r = min(r_begin + it * RPI + rsub, r_end - 1);
-    const int unit = r * LPR + jj;
+}
+
+// Build the operands of NT tokens (activation row of token t: row_of(t)) for
+// the LPR lane slots of a K-long row.  Caller synchronises.
+template <bool IS_Q8, int PARTS, bool SRC_F32, typename RowOf>
+BM_DEVICE void stage_x(uint4 *XL, const void *hi, const void *lo, int K, int NT, RowOf row_of) {
+  constexpr int XG = xgroups<PARTS>();
+  const int LPR = K / 64;
+  const int pieces = IS_Q8 ? 2 : 4;  // Q8: two 32-weight blocks; Q2: four sub-block slots
+  for (int idx = threadIdx.x; idx < NT * LPR * pieces; idx += blockDim.x) {
+    const int pc = idx % pieces, jj = (idx / pieces) % LPR, t = idx / (pieces * LPR);
+    const size_t row = size_t(row_of(t)) * K;
+    uint4 *base = XL + size_t(t) * XG * LPR + jj;
+    float sum = 0.f;
     if constexpr (IS_Q8) {
-      rg = q8_unit_load(a.sg + size_t(unit) * 68);
-      ru = q8_unit_load(a.su + size_t(unit) * 68);
+      const size_t off = row + jj * 64 + 32 * pc;
+#pragma unroll
+      for (int part = 0; part < PARTS; ++part) {
+        uint32_t d[16];
+        act_words<SRC_F32>(hi, lo, off, part, 32, d);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          base[(8 * part + 4 * pc + q) * LPR] = make_uint4(d[4 * q], d[4 * q + 1], d[4 * q + 2], d[4 * q + 3]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) sum = dot2_bf16(d[4 * q + w], BF16_ONEx2, sum);
+        }
+      }
+      reinterpret_cast<float *>(base + 8 * PARTS * LPR)[pc] = -128.f * sum;
     } else {
-      const int n = unit >> 2, q = unit & 3;
-      rg = q2_unit_load(a.wg + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
-      ru = q2_unit_load(a.wu + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+      const size_t off = row + q2_c0(jj >> 2, jj & 3, K) + 32 * pc;
+#pragma unroll
+      for (int part = 0; part < PARTS; ++part) {
+        uint32_t d[8], A[4], B[4];
+        act_words<SRC_F32>(hi, lo, off, part, 16, d);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w0 = d[2 * j], w1 = d[2 * j + 1];
+          A[j] = (w0 & 0xFFFFu) | (w1 << 16);
+          B[j] = (w0 >> 16) | (w1 & 0xFFFF0000u);
+          sum = dot2_bf16(w1, BF16_ONEx2, dot2_bf16(w0, BF16_ONEx2, sum));
+        }
+        base[(8 * part + pc) * LPR] = make_uint4(A[0], A[1], A[2], A[3]);
+        base[(8 * part + 4 + pc) * LPR] = make_uint4(B[0], B[1], B[2], B[3]);
+      }
+      reinterpret_cast<float *>(base + 8 * PARTS * LPR)[pc] = sum;
+      reinterpret_cast<float *>(base + (8 * PARTS + 1) * LPR)[pc] = -128.f * inv_f(pc) * sum;
     }
-  };
-  const int n_it = (r_end - r_begin + RPI - 1) / RPI;
-  // the wave's row iterations it = wave, wave + 4, ...: the weight loads of up
-  // to DEPTH of them are issued before any arithmetic, so their memory
-  // latencies overlap
-  constexpr int DEPTH = IS_Q8 ? 1 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));
-  for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
-    Raw rg[DEPTH], ru[DEPTH];
+  }
+}
+
+// Copy nbytes at src (4-byte aligned) into LDS at dst + (src & 15) with 16-byte
+// direct-to-LDS loads (each wave fills 64 consecutive 16-byte slots); returns
+// the byte offset src & 15.  The copy completes at s_waitcnt vmcnt(0).
+BM_DEVICE int stage_bytes(uint8_t *dst, const uint8_t *src, int nbytes) {
+  const int pad = int(reinterpret_cast<uintptr_t>(src) & 15u);
+  const uint8_t *base = src - pad;
+  const int n16 = (pad + nbytes + 15) >> 4;
+  const int lane = threadIdx.x & 63, wave0 = threadIdx.x & ~63;
+  for (int c0 = wave0; c0 < n16; c0 += blockDim.x) {
+    if (c0 + lane < n16)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(base + 16 * (c0 + lane)),
+                                       (__attribute__((address_space(3))) void *)(dst + 16 * c0),
+                                       16, 0, 0);
+  }
+  return pad;
+}
+
+BM_DEVICE uint32_t lds32(const uint8_t *p, int off) { return *reinterpret_cast<const uint32_t *>(p + off); }
+
+// Q2 units of NM matrices (LDS pointers at the units' super-blocks) against NT
+// tokens; out[m][t] += the unit's partial dot product.
+template <int NT, int PARTS, int NM>
+BM_DEVICE void q2_dot(const uint8_t *const (&sb)[NM], int h, int p, const uint4 *X, int LPR, float (&out)[NM][NT]) {
+  constexpr int XG = xgroups<PARTS>();
+  uint32_t w[NM][4], sw[NM][2];
+  float d[NM], dmin[NM];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (it0 + 4 * d < n_it) load_it(it0 + 4 * d, rg[d], ru[d]);
+  for (int m = 0; m < NM; ++m) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int it = it0 + 4 * d;
-      if (it >= n_it) break;
-      const int r = r_begin + it * RPI + rsub;
-      const bool active = r < r_end;
-      float g[NV], u[NV];
+    for (int i = 0; i < 4; ++i) w[m][i] = lds32(sb[m], 16 + 32 * h + 16 * p + 4 * i);
+    sw[m][0] = lds32(sb[m], 8 * h) >> (8 * p);
+    sw[m][1] = lds32(sb[m], 8 * h + 4) >> (8 * p);
+    const uint32_t dd = lds32(sb[m], 80);
+    d[m] = half_to_f32(dd & 0xFFFFu);
+    dmin[m] = half_to_f32(dd >> 16);
+  }
+  float yd[NM][NT], ym[NM][NT];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) g[v] = u[v] = 0.f;
-      if constexpr (IS_Q8) {
-        q8_unit_dot<NV>(rg[d], X, g);
-        q8_unit_dot<NV>(ru[d], X, u);
-      } else {
-        const int unit = (active ? r : r_end - 1) * LPR + jj;
-        q2_unit_dot<NV>(rg[d], unit & 1, X, g);
-        q2_unit_dot<NV>(ru[d], unit & 1, X, u);
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) yd[m][t] = ym[m][t] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 xa[NT][PARTS], xb[NT][PARTS];
+    float xs[NT], xc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int part = 0; part < PARTS; ++part) {
+        xa[t][part] = X[(t * XG + 8 * part + s) * LPR];
+        xb[t][part] = X[(t * XG + 8 * part + 4 + s) * LPR];
+      }
+      xs[t] = reinterpret_cast<const float *>(X + (t * XG + 8 * PARTS) * LPR)[s];
+      xc[t] = reinterpret_cast<const float *>(X + (t * XG + 8 * PARTS + 1) * LPR)[s];
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint32_t sbyte = (sw[m][s >> 1] >> (16 * (s & 1))) & 0xFFu;
+      const float scf = float(sbyte & 15u), mf = float(sbyte >> 4);
+      uint32_t A[4], B[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (s < 3) {
+          const uint32_t msk = 0x00030003u << (2 * s);
+          A[j] = and_or(w[m][j], msk, BF16_128x2);
+          B[j] = and_or(w[m][j] >> 8, msk, BF16_128x2);
+        } else {
+          A[j] = and_or(w[m][j] >> 2, 0x00300030u, BF16_128x2);
+          B[j] = and_or(w[m][j] >> 10, 0x00300030u, BF16_128x2);
+        }
       }
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float gs, us;
-        if constexpr (XF32) {
-          gs = g[2 * i] + g[2 * i + 1];
-          us = u[2 * i] + u[2 * i + 1];
-        } else {
-          gs = g[i];
-          us = u[i];
+      for (int t = 0; t < NT; ++t) {
+        float acc = 0.f;
+#pragma unroll
+        for (int part = 0; part < PARTS; ++part) {
+          acc = dot2_bf16(A[0], xa[t][part].x, acc);
+          acc = dot2_bf16(B[0], xb[t][part].x, acc);
+          acc = dot2_bf16(A[1], xa[t][part].y, acc);
+          acc = dot2_bf16(B[1], xb[t][part].y, acc);
+          acc = dot2_bf16(A[2], xa[t][part].z, acc);
+          acc = dot2_bf16(B[2], xb[t][part].z, acc);
+          acc = dot2_bf16(A[3], xa[t][part].w, acc);
+          acc = dot2_bf16(B[3], xb[t][part].w, acc);
         }
-        gs = lane_group_sum(gs, LPR);  // sum over the LPR lanes of the row
-        us = lane_group_sum(us, LPR);
-        if (active && jj == 0 && i < nt) {
+        const float qx = __builtin_fmaf(acc, inv_f(s), xc[t]);
+        yd[m][t] = __builtin_fmaf(scf, qx, yd[m][t]);
+        ym[m][t] = __builtin_fmaf(mf, xs[t], ym[m][t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[m][t] += d[m] * yd[m][t] - dmin[m] * ym[m][t];
+}
+
+// Q8_0 units (68 bytes: two 34-byte blocks) of NM matrices against NT tokens.
+template <int NT, int PARTS, int NM>
+BM_DEVICE void q8_dot(const uint8_t *const (&un)[NM], const uint4 *X, int LPR, float (&out)[NM][NT]) {
+  constexpr int XG = xgroups<PARTS>();
+  float acc[NM][2][NT];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][0][t] = acc[m][1][t] = 0.f;
+  float dA[NM], dB[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    dA[m] = half_to_f32(lds32(un[m], 0) & 0xFFFFu);
+    dB[m] = half_to_f32(lds32(un[m], 32) >> 16);
+  }
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint4 xp[NT][PARTS];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int part = 0; part < PARTS; ++part) xp[t][part] = X[(t * XG + 8 * part + 4 * b + g) * LPR];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        // codes 8g .. 8g+7 of block b: bytes 2 + 34b + 8g .. +7 of the unit
+        const int o = 2 + 34 * b + 8 * g;  // even; the dwords holding them start at o & ~3
+        const uint32_t u0 = lds32(un[m], o & ~3) ^ 0x80808080u, u1 = lds32(un[m], (o & ~3) + 4) ^ 0x80808080u,
+                       u2 = lds32(un[m], (o & ~3) + 8) ^ 0x80808080u;
+        const uint32_t uu[3] = {u0, u1, u2};
+        uint32_t pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b0 = (o & 3) + 2 * e, b1 = b0 + 1;  // byte index within uu (q + 128 as unsigned)
+          const float f0 = float((uu[b0 >> 2] >> (8 * (b0 & 3))) & 0xFFu);
+          const float f1 = float((uu[b1 >> 2] >> (8 * (b1 & 3))) & 0xFFu);
+          pr[e] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int part = 0; part < PARTS; ++part) {
+            acc[m][b][t] = dot2_bf16(pr[0], xp[t][part].x, acc[m][b][t]);
+            acc[m][b][t] = dot2_bf16(pr[1], xp[t][part].y, acc[m][b][t]);
+            acc[m][b][t] = dot2_bf16(pr[2], xp[t][part].z, acc[m][b][t]);
+            acc[m][b][t] = dot2_bf16(pr[3], xp[t][part].w, acc[m][b][t]);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float *xc = reinterpret_cast<const float *>(X + (t * XG + 8 * PARTS) * LPR);
+      out[m][t] += dA[m] * (acc[m][0][t] + xc[0]) + dB[m] * (acc[m][1][t] + xc[1]);
+    }
+}
+
+// One block of the gate/up (GATEUP) or down GEMV: rows [r0, r0 + nrows) of
+// the job for its tokens t0 .. t0 + nt - 1.  smem: weight bytes (NM matrices,
+// each at a 16-byte aligned offset, plus up to 12 bytes of lead), then the
+// activation operands.
+template <bool GATEUP, bool IS_Q8, int NT, bool XF32>
+BM_DEVICE void gemv_block(const FfnArgs &a, const Job &job, int t0, int nt, int r0, int nrows, uint8_t *smem) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int PARTS = GATEUP ? (XF32 ? 2 : 1) : 2;  // h always arrives as hi + lo
+  constexpr int XG = xgroups<PARTS>();
+  const int K = GATEUP ? a.D : a.F;
+  const int N = GATEUP ? a.F : a.D;
+  const int LPR = K / 64, RPI = 64 / LPR;
+  const size_t row_bytes = IS_Q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
+  const size_t mat_bytes = IS_Q8 ? 0 : size_t(a.F) * a.D / 256 * 84;
+  const uint8_t *mats[NM];
+  if constexpr (GATEUP) {
+    mats[0] = IS_Q8 ? a.sg : a.wg + size_t(job.e) * mat_bytes;
+    mats[NM - 1] = IS_Q8 ? a.su : a.wu + size_t(job.e) * mat_bytes;
+  } else {
+    mats[0] = IS_Q8 ? a.sd : a.wd + size_t(job.e) * mat_bytes;
+  }
+  const size_t chunk0 = size_t(r0) * row_bytes;  // chunk start inside a matrix
+  const int cbytes = int(size_t(nrows) * row_bytes);
+  const int stride = (cbytes + 16 + 15) & ~15;  // LDS bytes per matrix
+  uint4 *XL = reinterpret_cast<uint4 *>(smem + NM * stride);
+  __syncthreads();  // the previous pass is done with the block's LDS
+  int pad[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) pad[m] = stage_bytes(smem + m * stride, mats[m] + chunk0, cbytes);
+  if constexpr (GATEUP)
+    stage_x<IS_Q8, PARTS, XF32>(XL, a.x, a.x, K, NT, [&](int t) { return jtok(a, job, t0 + min(t, nt - 1)); });
+  else
+    stage_x<IS_Q8, PARTS, false>(XL, IS_Q8 ? a.hs : a.h, IS_Q8 ? a.hs_lo : a.h_lo, K, NT, [&](int t) {
+      return IS_Q8 ? jtok(a, job, t0 + min(t, nt - 1)) : jpair(job, t0 + min(t, nt - 1));
+    });
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int jj = lane % LPR, rsub = lane / LPR;
+  const uint4 *X = XL + jj;
+  const int n_it = (nrows + RPI - 1) / RPI;
+  for (int it = wave; it < n_it; it += 4) {
+    const int rl = it * RPI + rsub;  // row within the chunk
+    const bool active = rl < nrows;
+    const size_t unit = size_t(r0 + (active ? rl : nrows - 1)) * LPR + jj;
+    float acc[NM][NT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
+    if constexpr (IS_Q8) {
+      const uint8_t *un[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) un[m] = smem + m * stride + pad[m] + (unit * 68 - chunk0);
+      q8_dot<NT, PARTS, NM>(un, X, LPR, acc);
+    } else {
+      const uint8_t *sb[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) sb[m] = smem + m * stride + pad[m] + ((unit >> 2) * 84 - chunk0);
+      q2_dot<NT, PARTS, NM>(sb, int(unit >> 1) & 1, int(unit) & 1, X, LPR, acc);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = r0 + rl;
+      if constexpr (GATEUP) {
+        const float gs = lane_group_sum(acc[0][t], LPR);  // sum over the LPR lanes of the row
+        const float us = lane_group_sum(acc[NM - 1][t], LPR);
+        if (active && jj == 0 && t < nt) {
           const float hf = silu(gs) * us;
           const uint16_t hv = f32_to_bf16(hf);
-          const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + i)) * a.F + r : size_t(jpair(job, t0 + i)) * a.F + r;
+          const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + t)) * a.F + r : size_t(jpair(job, t0 + t)) * a.F + r;
           // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
           // rounding of h would dominate the layer's output error
           (IS_Q8 ? a.hs : a.h)[o] = hv;
           (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
         }
-      }
-    }
-  }
-}
-
-// Grid: the shared expert's row chunks first (its Q8_0 rows are the heaviest,
-// so they start first), then u_max routed job slots x chunks_gu row chunks.
-template <int NT, bool XF32>
-__global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
-  Job job;
-  int r_begin, r_end;
-  const bool shared = int(blockIdx.x) < a.chunks_sg;
-  if (shared) {
-    shared_job(a, job);
-    r_begin = blockIdx.x * a.rows_sg;
-    r_end = min(a.F, r_begin + a.rows_sg);
-  } else {
-    const int b = blockIdx.x - a.chunks_sg;
-    if (!pair_job(a, b / a.chunks_gu, job)) return;
-    r_begin = (b % a.chunks_gu) * a.rows_gu;
-    r_end = min(a.F, r_begin + a.rows_gu);
-  }
-  for (int t0 = 0; t0 < job.n; t0 += NT) {
-    const int nt = min(NT, job.n - t0);
-    if (shared)
-      gateup_rows<NT, XF32, true>(a, job, t0, nt, r_begin, r_end);
-    else
-      gateup_rows<NT, XF32, false>(a, job, t0, nt, r_begin, r_end);
-  }
-}
-
-// ---- down -------------------------------------------------------------------
-
-template <int NT, bool IS_Q8>
-BM_DEVICE void down_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r_begin, int r_end) {
-  constexpr bool XF32 = true;  // h always arrives as hi + lo parts
-  constexpr int NV = 2 * NT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int K = a.F, LPR = K / 64, RPI = 64 / LPR;
-  const int jj = lane % LPR, rsub = lane / LPR;
-  const int c0 = IS_Q8 ? jj * 64 : q2_c0(jj >> 2, jj & 3, K);
-  typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const size_t row = IS_Q8 ? size_t(jtok(a, job, t0 + min(i, nt - 1))) : size_t(jpair(job, t0 + min(i, nt - 1)));
-    const uint16_t *hi = (IS_Q8 ? a.hs : a.h) + row * K;
-    const uint16_t *lo = (IS_Q8 ? a.hs_lo : a.h_lo) + row * K;
-    if constexpr (IS_Q8) {
-      load_xq8_bf16(hi, c0, X[XF32 ? 2 * i : i]);
-      if constexpr (XF32) load_xq8_bf16(lo, c0, X[2 * i + 1]);
-    } else {
-      load_xq2_bf16(hi, c0, X[XF32 ? 2 * i : i]);
-      if constexpr (XF32) load_xq2_bf16(lo, c0, X[2 * i + 1]);
-    }
-  }
-  const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
-  using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
-  auto load_it = [&](int it, Raw &rw) {
-    const int r = min(r_begin + it * RPI + rsub, r_end - 1);
-    const int unit = r * LPR + jj;
-    if constexpr (IS_Q8) {
-      rw = q8_unit_load(a.sd + size_t(unit) * 68);
-    } else {
-      const int n = unit >> 2, q = unit & 3;
-      rw = q2_unit_load(a.wd + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
-    }
-  };
-  const int n_it = (r_end - r_begin + RPI - 1) / RPI;
-  constexpr int DEPTH = IS_Q8 ? 1 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));  // as in gate/up
-  for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
-    Raw rw[DEPTH];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (it0 + 4 * d < n_it) load_it(it0 + 4 * d, rw[d]);
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int it = it0 + 4 * d;
-      if (it >= n_it) break;
-      const int r = r_begin + it * RPI + rsub;
-      const bool active = r < r_end;
-      float y[NV];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) y[v] = 0.f;
-      if constexpr (IS_Q8) {
-        q8_unit_dot<NV>(rw[d], X, y);
       } else {
-        const int unit = (active ? r : r_end - 1) * LPR + jj;
-        q2_unit_dot<NV>(rw[d], unit & 1, X, y);
-      }
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float ys = XF32 ? y[2 * i] + y[2 * i + 1] : y[i];
-        ys = lane_group_sum(ys, LPR);
-        if (active && jj == 0 && i < nt) {
+        const float ys = lane_group_sum(acc[0][t], LPR);
+        if (active && jj == 0 && t < nt) {
           if constexpr (IS_Q8)
-            a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = ys;
+            a.ys[size_t(jtok(a, job, t0 + t)) * a.D + r] = ys;
           else
-            a.y[size_t(jpair(job, t0 + i)) * a.D + r] = ys;
+            a.y[size_t(jpair(job, t0 + t)) * a.D + r] = ys;
         }
       }
     }
   }
 }
 
-template <int NT>
-__global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
+// Grid: the shared expert's row chunks first, then u_max routed job slots x
+// row chunks; every job's tokens in passes of NT.
+template <bool GATEUP, int NT, bool XF32>
+__global__ void __launch_bounds__(256) ffn_gemv_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_gemv[];
   Job job;
-  int r_begin, r_end;
-  const bool shared = int(blockIdx.x) < a.chunks_sd;
+  const int n_sh = GATEUP ? a.chunks_sg : a.chunks_sd;
+  const int rows_sh = GATEUP ? a.rows_sg : a.rows_sd;
+  const int rows_rt = GATEUP ? a.rows_gu : a.rows_dn;
+  const int chunks_rt = GATEUP ? a.chunks_gu : a.chunks_dn;
+  const int N = GATEUP ? a.F : a.D;
+  const bool shared = int(blockIdx.x) < n_sh;
+  int r0, nrows;
   if (shared) {
     shared_job(a, job);
-    r_begin = blockIdx.x * a.rows_sd;
-    r_end = min(a.D, r_begin + a.rows_sd);
+    r0 = blockIdx.x * rows_sh;
+    nrows = min(rows_sh, N - r0);
   } else {
-    const int b = blockIdx.x - a.chunks_sd;
-    if (!pair_job(a, b / a.chunks_dn, job)) return;
-    r_begin = (b % a.chunks_dn) * a.rows_dn;
-    r_end = min(a.D, r_begin + a.rows_dn);
+    const int b = blockIdx.x - n_sh;
+    if (!pair_job(a, b / chunks_rt, job)) return;
+    r0 = (b % chunks_rt) * rows_rt;
+    nrows = min(rows_rt, N - r0);
   }
   for (int t0 = 0; t0 < job.n; t0 += NT) {
     const int nt = min(NT, job.n - t0);
     if (shared)
-      down_rows<NT, true>(a, job, t0, nt, r_begin, r_end);
+      gemv_block<GATEUP, true, NT, XF32>(a, job, t0, nt, r0, nrows, smem_gemv);
     else
-      down_rows<NT, false>(a, job, t0, nt, r_begin, r_end);
+      gemv_block<GATEUP, false, NT, XF32>(a, job, t0, nt, r0, nrows, smem_gemv);
   }
+}
+
+// LDS bytes of a GEMV launch: NM matrices of `rows` rows plus the operands
+static size_t gemv_smem(bool gateup, bool q8, int K, int rows, int nt, int parts) {
+  const size_t row_bytes = q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
+  const size_t stride = (size_t(rows) * row_bytes + 16 + 15) & ~size_t(15);
+  return (gateup ? 2 : 1) * stride + size_t(nt) * (8 * parts + 2) * (K / 64) * 16;
+}
+
+// ---- GEMV launch configuration -------------------------------------------------
+
+// Rows per block: multiples of 4 waves x RPI rows, sized so that the block's
+// weight bytes plus its activation operands fit a 60 KB LDS budget (at least
+// one wave iteration, at most four).
+static int gemv_rows(bool gateup, bool q8, int K, int N, int nt, int parts) {
+  const int LPR = K / 64, RPI = 64 / LPR;
+  const size_t row_bytes = q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
+  const size_t x_bytes = size_t(nt) * (8 * parts + 2) * LPR * 16;
+  const size_t budget = 60 * 1024 > x_bytes + 4096 ? 60 * 1024 - x_bytes : 4096;
+  const size_t per_iter = size_t(gateup ? 2 : 1) * 4 * RPI * row_bytes;
+  const int iters = int(std::max<size_t>(1, std::min<size_t>(4, budget / per_iter)));
+  return std::min(N, 4 * RPI * iters);
+}
+
+// One GEMV launch (gate/up or down) over `nshared` shared-expert chunks and
+// u_max routed job slots; raises the kernel's LDS limit when needed.
+template <bool GATEUP, int NT, bool XF32>
+static hipError_t launch_gemv(FfnArgs a, bool with_routed, hipStream_t stream) {
+  constexpr int PARTS = GATEUP ? (XF32 ? 2 : 1) : 2;
+  const int K = GATEUP ? a.D : a.F, N = GATEUP ? a.F : a.D;
+  const bool has_shared = GATEUP ? a.sg != nullptr : a.sd != nullptr;
+  const int rows_rt = gemv_rows(GATEUP, false, K, N, NT, PARTS);
+  const int rows_sh = gemv_rows(GATEUP, true, K, N, NT, PARTS);
+  const int chunks_rt = (N + rows_rt - 1) / rows_rt, chunks_sh = has_shared ? (N + rows_sh - 1) / rows_sh : 0;
+  if (GATEUP) {
+    a.rows_gu = rows_rt;
+    a.chunks_gu = chunks_rt;
+    a.rows_sg = rows_sh;
+    a.chunks_sg = chunks_sh;
+  } else {
+    a.rows_dn = rows_rt;
+    a.chunks_dn = chunks_rt;
+    a.rows_sd = rows_sh;
+    a.chunks_sd = chunks_sh;
+  }
+  if (!with_routed) a.u_max = 0;
+  const size_t smem = std::max(with_routed ? gemv_smem(GATEUP, false, K, rows_rt, NT, PARTS) : 0,
+                               has_shared ? gemv_smem(GATEUP, true, K, rows_sh, NT, PARTS) : 0);
+  const unsigned grid = unsigned(chunks_sh + a.u_max * chunks_rt);
+  if (grid == 0) return hipSuccess;
+  if (smem > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_gemv_kernel<GATEUP, NT, XF32>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+  }
+  BM_LAUNCH(GATEUP ? "ffn_gateup_kernel" : "ffn_down_kernel", (ffn_gemv_kernel<GATEUP, NT, XF32>), dim3(grid),
+            dim3(256), smem, stream, a);
+  return hipGetLastError();
 }
 
 // ---- routed experts on MFMA (decode) ------------------------------------------
@@ -692,8 +693,6 @@ static size_t mfma_decode_smem(int K, int np, int parts) {
 template <int NT, bool XF32>
 static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
   const size_t cap = 56 * 1024;
-  FfnArgs sh = a;
-  sh.u_max = 0;  // shared row chunks only
   hipError_t err;
   {  // gate/up
     const int parts = XF32 ? 2 : 1;
@@ -703,10 +702,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
     BM_LAUNCH("ffn_mfma_gateup_kernel", (ffn_mfma_decode_kernel<true, XF32>), dim3(a.u_max * (a.F / 16)), dim3(256),
               mfma_decode_smem(a.D, c.np, parts), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sg) {
-      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(a.chunks_sg), dim3(256), 0, stream, sh);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+    if (a.sg && (err = launch_gemv<true, NT, XF32>(a, false, stream)) != hipSuccess) return err;
   }
   {  // down
     const size_t per_row = size_t(2) * a.F * 2 + size_t(a.F / 256) * 64;
@@ -715,10 +711,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
     BM_LAUNCH("ffn_mfma_down_kernel", (ffn_mfma_decode_kernel<false, XF32>), dim3(a.u_max * (a.D / 16)), dim3(256),
               mfma_decode_smem(a.F, c.np, 2), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sd) {
-      BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<(NT > 2 ? 2 : NT)>), dim3(a.chunks_sd), dim3(256), 0, stream, sh);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+    if (a.sd && (err = launch_gemv<false, (NT > 2 ? 2 : NT), false>(a, false, stream)) != hipSuccess) return err;
   }
   return hipSuccess;
 }
@@ -766,36 +759,16 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 
 // ---- launch -----------------------------------------------------------------
 
-template <int NT_GU, int NT_DN>
-static hipError_t launch_decode_nt(const FfnArgs &a, bool xf32, hipStream_t stream) {
-  dim3 g1(a.chunks_sg + a.u_max * a.chunks_gu), g2(a.chunks_sd + a.u_max * a.chunks_dn);
-  if (xf32)
-    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_GU, true>), g1, dim3(256), 0, stream, a);
-  else
-    BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_GU, false>), g1, dim3(256), 0, stream, a);
-  hipError_t err = hipGetLastError();
+template <int NT_GU, int NT_DN, bool XF32>
+static hipError_t launch_decode_nt(const FfnArgs &a, hipStream_t stream) {
+  hipError_t err = launch_gemv<true, NT_GU, XF32>(a, true, stream);
   if (err != hipSuccess) return err;
-  BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT_DN>), g2, dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_gemv<false, NT_DN, false>(a, true, stream);
 }
 
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
-  // rows per block: 4 row-iterations (64/LPR rows each) per wave, so every
-  // wave reuses its activation registers over several rows
-  const int rpi_gu = 64 / (a.D / 64), rpi_dn = 64 / (a.F / 64);
   const bool mfma = a.T >= 3 && a.D % 256 == 0 && a.F % 256 == 0;
-  a.rows_gu = min(a.F, 16 * rpi_gu);
-  a.rows_dn = min(a.D, 16 * rpi_dn);
-  a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
-  a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
-  // shared expert: one row iteration per wave, since a Q8_0 row is 3.2x the
-  // bytes of a 2-bit row; its blocks then carry about as many bytes as a routed one
-  a.rows_sg = min(a.F, 4 * rpi_gu);
-  a.rows_sd = min(a.D, 4 * rpi_dn);
-  a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
-  a.chunks_sd = a.sd ? (a.D + a.rows_sd - 1) / a.rows_sd : 0;
   a.u_max = a.T * a.k;  // one job slot per pair; repeated experts exit at once
-  // tokens held in registers per pass (a job's tokens beyond that take more passes)
   hipError_t err;
   if (mfma) {
     // routed experts on MFMA, shared expert on the GEMV rows of the same launches
@@ -805,12 +778,13 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
       err = xf32 ? launch_mfma_decode<2, true>(a, stream) : launch_mfma_decode<2, false>(a, stream);
     else
       err = launch_mfma_decode<NTOK, false>(a, stream);
-  } else if (a.T == 1)
-    err = launch_decode_nt<1, 1>(a, xf32, stream);
-  else if (a.T == 2 || xf32)
-    err = launch_decode_nt<2, 2>(a, xf32, stream);
-  else
-    err = launch_decode_nt<NTOK, 2>(a, xf32, stream);
+  } else if (a.T == 1) {
+    err = xf32 ? launch_decode_nt<1, 1, true>(a, stream) : launch_decode_nt<1, 1, false>(a, stream);
+  } else if (a.T == 2 || xf32) {
+    err = xf32 ? launch_decode_nt<2, 2, true>(a, stream) : launch_decode_nt<2, 2, false>(a, stream);
+  } else {
+    err = launch_decode_nt<NTOK, 2, false>(a, stream);
+  }
   if (err != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
                         stream);
