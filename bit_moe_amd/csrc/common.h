@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #define BM_DEVICE __device__ __forceinline__
+#define BM_HOST_DEVICE __host__ __device__
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;

@@ -319,41 +319,25 @@ BM_DEVICE void q8_dot(const uint8_t *const (&un)[NM], const uint4 *X, int LPR, f
     }
 }
 
-// One block of the gate/up (GATEUP) or down GEMV: rows [r0, r0 + nrows) of
-// the job for its tokens t0 .. t0 + nt - 1.  smem: weight bytes (NM matrices,
-// each at a 16-byte aligned offset, plus up to 12 bytes of lead), then the
-// activation operands.
-template <bool GATEUP, bool IS_Q8, int NT, bool XF32>
-BM_DEVICE void gemv_block(const FfnArgs &a, const Job &job, int t0, int nt, int r0, int nrows, uint8_t *smem) {
-  constexpr int NM = GATEUP ? 2 : 1;
-  constexpr int PARTS = GATEUP ? (XF32 ? 2 : 1) : 2;  // h always arrives as hi + lo
-  constexpr int XG = xgroups<PARTS>();
-  const int K = GATEUP ? a.D : a.F;
-  const int N = GATEUP ? a.F : a.D;
-  const int LPR = K / 64, RPI = 64 / LPR;
+// One block of the down GEMV: rows [r0, r0 + nrows) of the job's down matrix
+// for its pairs (shared expert: tokens) t0 .. t0 + nt - 1.  smem: the rows'
+// weight bytes (plus up to 12 bytes of lead), then the activation operands
+// (h as hi + lo parts).
+template <bool IS_Q8, int NT>
+BM_DEVICE void down_block(const FfnArgs &a, const Job &job, int t0, int nt, int r0, int nrows, uint8_t *smem) {
+  constexpr int PARTS = 2;
+  const int K = a.F, LPR = K / 64, RPI = 64 / LPR;
   const size_t row_bytes = IS_Q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
-  const size_t mat_bytes = IS_Q8 ? 0 : size_t(a.F) * a.D / 256 * 84;
-  const uint8_t *mats[NM];
-  if constexpr (GATEUP) {
-    mats[0] = IS_Q8 ? a.sg : a.wg + size_t(job.e) * mat_bytes;
-    mats[NM - 1] = IS_Q8 ? a.su : a.wu + size_t(job.e) * mat_bytes;
-  } else {
-    mats[0] = IS_Q8 ? a.sd : a.wd + size_t(job.e) * mat_bytes;
-  }
-  const size_t chunk0 = size_t(r0) * row_bytes;  // chunk start inside a matrix
+  const uint8_t *mat = IS_Q8 ? a.sd : a.wd + size_t(job.e) * (size_t(a.F) * a.D / 256 * 84);
+  const size_t chunk0 = size_t(r0) * row_bytes;  // chunk start inside the matrix
   const int cbytes = int(size_t(nrows) * row_bytes);
-  const int stride = (cbytes + 16 + 15) & ~15;  // LDS bytes per matrix
-  uint4 *XL = reinterpret_cast<uint4 *>(smem + NM * stride);
+  const int stride = (cbytes + 16 + 15) & ~15;
+  uint4 *XL = reinterpret_cast<uint4 *>(smem + stride);
   __syncthreads();  // the previous pass is done with the block's LDS
-  int pad[NM];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) pad[m] = stage_bytes(smem + m * stride, mats[m] + chunk0, cbytes);
-  if constexpr (GATEUP)
-    stage_x<IS_Q8, PARTS, XF32>(XL, a.x, a.x, K, NT, [&](int t) { return jtok(a, job, t0 + min(t, nt - 1)); });
-  else
-    stage_x<IS_Q8, PARTS, false>(XL, IS_Q8 ? a.hs : a.h, IS_Q8 ? a.hs_lo : a.h_lo, K, NT, [&](int t) {
-      return IS_Q8 ? jtok(a, job, t0 + min(t, nt - 1)) : jpair(job, t0 + min(t, nt - 1));
-    });
+  const int pad = stage_bytes(smem, mat + chunk0, cbytes);
+  stage_x<IS_Q8, PARTS, false>(XL, IS_Q8 ? a.hs : a.h, IS_Q8 ? a.hs_lo : a.h_lo, K, NT, [&](int t) {
+    return IS_Q8 ? jtok(a, job, t0 + min(t, nt - 1)) : jpair(job, t0 + min(t, nt - 1));
+  });
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -364,137 +348,456 @@ BM_DEVICE void gemv_block(const FfnArgs &a, const Job &job, int t0, int nt, int 
     const int rl = it * RPI + rsub;  // row within the chunk
     const bool active = rl < nrows;
     const size_t unit = size_t(r0 + (active ? rl : nrows - 1)) * LPR + jj;
-    float acc[NM][NT];
+    float acc[1][NT];
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
+    for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
     if constexpr (IS_Q8) {
-      const uint8_t *un[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) un[m] = smem + m * stride + pad[m] + (unit * 68 - chunk0);
-      q8_dot<NT, PARTS, NM>(un, X, LPR, acc);
+      const uint8_t *un[1] = {smem + pad + (unit * 68 - chunk0)};
+      q8_dot<NT, PARTS, 1>(un, X, LPR, acc);
     } else {
-      const uint8_t *sb[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) sb[m] = smem + m * stride + pad[m] + ((unit >> 2) * 84 - chunk0);
-      q2_dot<NT, PARTS, NM>(sb, int(unit >> 1) & 1, int(unit) & 1, X, LPR, acc);
+      const uint8_t *sb[1] = {smem + pad + ((unit >> 2) * 84 - chunk0)};
+      q2_dot<NT, PARTS, 1>(sb, int(unit >> 1) & 1, int(unit) & 1, X, LPR, acc);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int r = r0 + rl;
-      if constexpr (GATEUP) {
-        const float gs = lane_group_sum(acc[0][t], LPR);  // sum over the LPR lanes of the row
-        const float us = lane_group_sum(acc[NM - 1][t], LPR);
-        if (active && jj == 0 && t < nt) {
-          const float hf = silu(gs) * us;
-          const uint16_t hv = f32_to_bf16(hf);
-          const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + t)) * a.F + r : size_t(jpair(job, t0 + t)) * a.F + r;
-          // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
-          // rounding of h would dominate the layer's output error
-          (IS_Q8 ? a.hs : a.h)[o] = hv;
-          (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
-        }
-      } else {
-        const float ys = lane_group_sum(acc[0][t], LPR);
-        if (active && jj == 0 && t < nt) {
-          if constexpr (IS_Q8)
-            a.ys[size_t(jtok(a, job, t0 + t)) * a.D + r] = ys;
-          else
-            a.y[size_t(jpair(job, t0 + t)) * a.D + r] = ys;
-        }
+      const float ys = lane_group_sum(acc[0][t], LPR);  // sum over the LPR lanes of the row
+      if (active && jj == 0 && t < nt) {
+        const int r = r0 + rl;
+        if constexpr (IS_Q8)
+          a.ys[size_t(jtok(a, job, t0 + t)) * a.D + r] = ys;
+        else
+          a.y[size_t(jpair(job, t0 + t)) * a.D + r] = ys;
       }
     }
   }
 }
 
 // Grid: the shared expert's row chunks first, then u_max routed job slots x
-// row chunks; every job's tokens in passes of NT.
-template <bool GATEUP, int NT, bool XF32>
-__global__ void __launch_bounds__(256) ffn_gemv_kernel(FfnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem_gemv[];
+// row chunks; every job's pairs in passes of NT.
+template <int NT>
+__global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_down[];
   Job job;
-  const int n_sh = GATEUP ? a.chunks_sg : a.chunks_sd;
-  const int rows_sh = GATEUP ? a.rows_sg : a.rows_sd;
-  const int rows_rt = GATEUP ? a.rows_gu : a.rows_dn;
-  const int chunks_rt = GATEUP ? a.chunks_gu : a.chunks_dn;
-  const int N = GATEUP ? a.F : a.D;
-  const bool shared = int(blockIdx.x) < n_sh;
+  const bool shared = int(blockIdx.x) < a.chunks_sd;
   int r0, nrows;
   if (shared) {
     shared_job(a, job);
-    r0 = blockIdx.x * rows_sh;
-    nrows = min(rows_sh, N - r0);
+    r0 = blockIdx.x * a.rows_sd;
+    nrows = min(a.rows_sd, a.D - r0);
   } else {
-    const int b = blockIdx.x - n_sh;
-    if (!pair_job(a, b / chunks_rt, job)) return;
-    r0 = (b % chunks_rt) * rows_rt;
-    nrows = min(rows_rt, N - r0);
+    const int b = blockIdx.x - a.chunks_sd;
+    if (!pair_job(a, b / a.chunks_dn, job)) return;
+    r0 = (b % a.chunks_dn) * a.rows_dn;
+    nrows = min(a.rows_dn, a.D - r0);
   }
   for (int t0 = 0; t0 < job.n; t0 += NT) {
     const int nt = min(NT, job.n - t0);
     if (shared)
-      gemv_block<GATEUP, true, NT, XF32>(a, job, t0, nt, r0, nrows, smem_gemv);
+      down_block<true, NT>(a, job, t0, nt, r0, nrows, smem_down);
     else
-      gemv_block<GATEUP, false, NT, XF32>(a, job, t0, nt, r0, nrows, smem_gemv);
+      down_block<false, NT>(a, job, t0, nt, r0, nrows, smem_down);
   }
 }
 
-// LDS bytes of a GEMV launch: NM matrices of `rows` rows plus the operands
-static size_t gemv_smem(bool gateup, bool q8, int K, int rows, int nt, int parts) {
-  const size_t row_bytes = q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
-  const size_t stride = (size_t(rows) * row_bytes + 16 + 15) & ~size_t(15);
-  return (gateup ? 2 : 1) * stride + size_t(nt) * (8 * parts + 2) * (K / 64) * 16;
+// ---- gate/up GEMV: activation operands in registers -----------------------------
+// Every lane keeps its unit's operands (x pairs in code-byte order, sub-block
+// sums) in registers for all the rows it visits; the weight bytes of up to
+// DEPTH row iterations are loaded before any arithmetic.
+
+struct XQ2 {  // one bf16 "virtual token" for one Q2 unit
+  uint32_t a[16], b[16];
+  float sum[4], c[4];
+};
+
+
+
+BM_DEVICE void xq2_finish(XQ2 &X) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) X.c[s] = -128.f * inv_f(s) * X.sum[s];
 }
 
-// ---- GEMV launch configuration -------------------------------------------------
+BM_DEVICE void xq2_from_words(XQ2 &X, int s, const uint32_t (&d)[8]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = d[2 * j], hi = d[2 * j + 1];
+    X.a[4 * s + j] = (lo & 0xFFFFu) | (hi << 16);
+    X.b[4 * s + j] = (lo >> 16) | (hi & 0xFFFF0000u);
+    sum = dot2_bf16(hi, BF16_ONEx2, dot2_bf16(lo, BF16_ONEx2, sum));
+  }
+  X.sum[s] = sum;
+}
 
-// Rows per block: multiples of 4 waves x RPI rows, sized so that the block's
-// weight bytes plus its activation operands fit a 60 KB LDS budget (at least
-// one wave iteration, at most four).
-static int gemv_rows(bool gateup, bool q8, int K, int N, int nt, int parts) {
+// bf16 activations: 16 contiguous values at row + c0 + 32 s
+BM_DEVICE void load_xq2_bf16(const uint16_t *row, int c0, XQ2 &X) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(row + c0 + 32 * s);
+    const uint4 v0 = p[0], v1 = p[1];
+    const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    xq2_from_words(X, s, d);
+  }
+  xq2_finish(X);
+}
+
+// float32 activations: split exactly enough into bf16 hi + bf16 lo parts
+// (x - hi is exact in float32), two virtual tokens whose results are summed.
+BM_DEVICE void load_xq2_f32(const float *row, int c0, XQ2 &Xh, XQ2 &Xl) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const float4 *p = reinterpret_cast<const float4 *>(row + c0 + 32 * s);
+    uint32_t dh[8], dl[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = p[q];
+      const float f[4] = {v.x, v.y, v.z, v.w};
+      uint32_t hb[4], lb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = f32_to_bf16(f[i]);
+        lb[i] = f32_to_bf16(f[i] - bf16_to_f32(uint16_t(hb[i])));
+      }
+      dh[2 * q] = hb[0] | (hb[1] << 16);
+      dh[2 * q + 1] = hb[2] | (hb[3] << 16);
+      dl[2 * q] = lb[0] | (lb[1] << 16);
+      dl[2 * q + 1] = lb[2] | (lb[3] << 16);
+    }
+    xq2_from_words(Xh, s, dh);
+    xq2_from_words(Xl, s, dl);
+  }
+  xq2_finish(Xh);
+  xq2_finish(Xl);
+}
+
+struct XQ8 {  // one bf16 virtual token for one Q8_0 unit (two 32-weight blocks)
+  uint32_t p[32];
+  float c[2];
+};
+
+BM_DEVICE void load_xq8_bf16(const uint16_t *row, int c0, XQ8 &X) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(row + c0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = p[4 * b + q];
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        X.p[16 * b + 4 * q + i] = d[i];
+        sum = dot2_bf16(d[i], BF16_ONEx2, sum);
+      }
+    }
+    X.c[b] = -128.f * sum;
+  }
+}
+
+BM_DEVICE void load_xq8_f32(const float *row, int c0, XQ8 &Xh, XQ8 &Xl) {
+  const float4 *p = reinterpret_cast<const float4 *>(row + c0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    float sh = 0.f, sl = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = p[8 * b + q];
+      const float f[4] = {v.x, v.y, v.z, v.w};
+      uint32_t hb[4], lb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = f32_to_bf16(f[i]);
+        const float hf = bf16_to_f32(uint16_t(hb[i]));
+        lb[i] = f32_to_bf16(f[i] - hf);
+        sh += hf;
+        sl += bf16_to_f32(uint16_t(lb[i]));
+      }
+      Xh.p[16 * b + 2 * q] = hb[0] | (hb[1] << 16);
+      Xh.p[16 * b + 2 * q + 1] = hb[2] | (hb[3] << 16);
+      Xl.p[16 * b + 2 * q] = lb[0] | (lb[1] << 16);
+      Xl.p[16 * b + 2 * q + 1] = lb[2] | (lb[3] << 16);
+    }
+    Xh.c[b] = -128.f * sh;
+    Xl.c[b] = -128.f * sl;
+  }
+}
+
+// ---- one row unit against NV virtual tokens ----------------------------------
+
+struct Q2Unit {  // raw bytes of one lane's quarter super-block
+  u32x4 q;
+  u32x2 sc;
+  uint32_t dd;
+};
+
+BM_DEVICE Q2Unit q2_unit_load(const uint8_t *sb, int h, int p) {
+  Q2Unit r;
+  r.q = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * h + 16 * p);
+  r.sc = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * h);
+  r.dd = *reinterpret_cast<const uint32_t *>(sb + 80);
+  return r;
+}
+
+template <int NV>
+BM_DEVICE void q2_unit_dot(const Q2Unit &u, int p, const XQ2 *X, float *out) {
+  const float d = half_to_f32(u.dd & 0xFFFFu), dmin = half_to_f32(u.dd >> 16);
+  const uint32_t w[4] = {u.q.x, u.q.y, u.q.z, u.q.w};
+  const uint32_t sw0 = u.sc.x >> (8 * p), sw1 = u.sc.y >> (8 * p);
+  float yd[NV], ym[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) yd[v] = ym[v] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t sbyte = ((s < 2 ? sw0 : sw1) >> (16 * (s & 1))) & 0xFFu;
+    const float scf = float(sbyte & 15u), mf = float(sbyte >> 4);
+    float acc[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t A, B;
+      if (s < 3) {
+        const uint32_t m = 0x00030003u << (2 * s);
+        A = and_or(w[j], m, BF16_128x2);
+        B = and_or(w[j] >> 8, m, BF16_128x2);
+      } else {
+        A = and_or(w[j] >> 2, 0x00300030u, BF16_128x2);
+        B = and_or(w[j] >> 10, 0x00300030u, BF16_128x2);
+      }
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        acc[v] = dot2_bf16(A, X[v].a[4 * s + j], acc[v]);
+        acc[v] = dot2_bf16(B, X[v].b[4 * s + j], acc[v]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const float qx = __builtin_fmaf(acc[v], inv_f(s), X[v].c[s]);
+      yd[v] = __builtin_fmaf(scf, qx, yd[v]);
+      ym[v] = __builtin_fmaf(mf, X[v].sum[s], ym[v]);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) out[v] += d * yd[v] - dmin * ym[v];
+}
+
+struct Q8Unit {  // raw bytes of one lane's two Q8_0 blocks (68 bytes)
+  uint32_t dw[17];
+};
+
+BM_DEVICE Q8Unit q8_unit_load(const uint8_t *u68) {
+  Q8Unit r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = *reinterpret_cast<const u32x4_a4 *>(u68 + 16 * i);
+    r.dw[4 * i] = v.x;
+    r.dw[4 * i + 1] = v.y;
+    r.dw[4 * i + 2] = v.z;
+    r.dw[4 * i + 3] = v.w;
+  }
+  r.dw[16] = *reinterpret_cast<const uint32_t *>(u68 + 64);
+  return r;
+}
+
+template <int NV>
+BM_DEVICE void q8_unit_dot(const Q8Unit &u, const XQ8 *X, float *out) {
+  const float dA = half_to_f32(u.dw[0] & 0xFFFFu), dB = half_to_f32(u.dw[8] >> 16);
+  uint32_t ux[17];
+#pragma unroll
+  for (int i = 0; i < 17; ++i) ux[i] = u.dw[i] ^ 0x80808080u;  // q + 128 as unsigned bytes
+  float acc[2][NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) acc[0][v] = acc[1][v] = 0.f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int i = 0; i < 32; i += 2) {
+      const int byte0 = (b ? 36 : 2) + i;  // byte offset of q_i inside the 68-byte unit
+      const int byte1 = byte0 + 1;
+      const float f0 = float((ux[byte0 >> 2] >> (8 * (byte0 & 3))) & 0xFFu);
+      const float f1 = float((ux[byte1 >> 2] >> (8 * (byte1 & 3))) & 0xFFu);
+      const uint32_t pr = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[b][v] = dot2_bf16(pr, X[v].p[16 * b + i / 2], acc[b][v]);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) out[v] += dA * (acc[0][v] + X[v].c[0]) + dB * (acc[1][v] + X[v].c[1]);
+}
+
+// ---- gate/up ----------------------------------------------------------------
+
+// Rows [r_begin, r_end) of one job for tokens t0 .. t0+nt-1 of the job.
+// IS_Q8: shared expert (Q8_0) instead of a routed expert (Q2).
+template <int NT, bool XF32, bool IS_Q8>
+BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r_begin, int r_end) {
+  constexpr int NV = XF32 ? 2 * NT : NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = a.D, LPR = K / 64, RPI = 64 / LPR;
+  const int jj = lane % LPR, rsub = lane / LPR;
+  // the lane's columns do not depend on the row: K is a multiple of 128
+  const int c0 = IS_Q8 ? jj * 64 : q2_c0(jj >> 2, jj & 3, K);
+  typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int t = jtok(a, job, t0 + min(i, nt - 1));
+    if constexpr (IS_Q8) {
+      if constexpr (XF32)
+        load_xq8_f32(static_cast<const float *>(a.x) + size_t(t) * K, c0, X[2 * i], X[2 * i + 1]);
+      else
+        load_xq8_bf16(static_cast<const uint16_t *>(a.x) + size_t(t) * K, c0, X[i]);
+    } else {
+      if constexpr (XF32)
+        load_xq2_f32(static_cast<const float *>(a.x) + size_t(t) * K, c0, X[2 * i], X[2 * i + 1]);
+      else
+        load_xq2_bf16(static_cast<const uint16_t *>(a.x) + size_t(t) * K, c0, X[i]);
+    }
+  }
+  const size_t mat_bytes_q2 = size_t(a.F) * a.D / 256 * 84;
+  using Raw = typename std::conditional<IS_Q8, Q8Unit, Q2Unit>::type;
+  // raw bytes of the lane's unit in row iteration `it`
+  auto load_it = [&](int it, Raw &rg, Raw &ru) {
+    const int r = min(r_begin + it * RPI + rsub, r_end - 1);
+    const int unit = r * LPR + jj;
+    if constexpr (IS_Q8) {
+      rg = q8_unit_load(a.sg + size_t(unit) * 68);
+      ru = q8_unit_load(a.su + size_t(unit) * 68);
+    } else {
+      const int n = unit >> 2, q = unit & 3;
+      rg = q2_unit_load(a.wg + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+      ru = q2_unit_load(a.wu + size_t(job.e) * mat_bytes_q2 + size_t(n) * 84, q >> 1, q & 1);
+    }
+  };
+  const int n_it = (r_end - r_begin + RPI - 1) / RPI;
+  // the wave's row iterations it = wave, wave + 4, ...: the weight loads of up
+  // to DEPTH of them are issued before any arithmetic, so their memory
+  // latencies overlap
+  constexpr int DEPTH = IS_Q8 ? 2 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));
+  for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
+    Raw rg[DEPTH], ru[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (it0 + 4 * d < n_it) load_it(it0 + 4 * d, rg[d], ru[d]);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = it0 + 4 * d;
+      if (it >= n_it) break;
+      const int r = r_begin + it * RPI + rsub;
+      const bool active = r < r_end;
+      float g[NV], u[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) g[v] = u[v] = 0.f;
+      if constexpr (IS_Q8) {
+        q8_unit_dot<NV>(rg[d], X, g);
+        q8_unit_dot<NV>(ru[d], X, u);
+      } else {
+        const int unit = (active ? r : r_end - 1) * LPR + jj;
+        q2_unit_dot<NV>(rg[d], unit & 1, X, g);
+        q2_unit_dot<NV>(ru[d], unit & 1, X, u);
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float gs, us;
+        if constexpr (XF32) {
+          gs = g[2 * i] + g[2 * i + 1];
+          us = u[2 * i] + u[2 * i + 1];
+        } else {
+          gs = g[i];
+          us = u[i];
+        }
+        gs = lane_group_sum(gs, LPR);  // sum over the LPR lanes of the row
+        us = lane_group_sum(us, LPR);
+        if (active && jj == 0 && i < nt) {
+          const float hf = silu(gs) * us;
+          const uint16_t hv = f32_to_bf16(hf);
+          const size_t o = IS_Q8 ? size_t(jtok(a, job, t0 + i)) * a.F + r : size_t(jpair(job, t0 + i)) * a.F + r;
+          // h travels as bf16 hi + lo parts (16 significant bits): a single bf16
+          // rounding of h would dominate the layer's output error
+          (IS_Q8 ? a.hs : a.h)[o] = hv;
+          (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(hf - bf16_to_f32(hv));
+        }
+      }
+    }
+  }
+}
+
+// Grid: the shared expert's row chunks first (its Q8_0 rows are the heaviest,
+// so they start first), then u_max routed job slots x chunks_gu row chunks.
+template <int NT, bool XF32>
+__global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
+  Job job;
+  int r_begin, r_end;
+  const bool shared = int(blockIdx.x) < a.chunks_sg;
+  if (shared) {
+    shared_job(a, job);
+    r_begin = blockIdx.x * a.rows_sg;
+    r_end = min(a.F, r_begin + a.rows_sg);
+  } else {
+    const int b = blockIdx.x - a.chunks_sg;
+    if (!pair_job(a, b / a.chunks_gu, job)) return;
+    r_begin = (b % a.chunks_gu) * a.rows_gu;
+    r_end = min(a.F, r_begin + a.rows_gu);
+  }
+  for (int t0 = 0; t0 < job.n; t0 += NT) {
+    const int nt = min(NT, job.n - t0);
+    if (shared)
+      gateup_rows<NT, XF32, true>(a, job, t0, nt, r_begin, r_end);
+    else
+      gateup_rows<NT, XF32, false>(a, job, t0, nt, r_begin, r_end);
+  }
+}
+
+// ---- launch configuration -----------------------------------------------------
+
+// Down rows per block (a multiple of 4 waves x RPI rows) sized so that the
+// rows' bytes plus the activation operands fit a 44 KB LDS budget (at least
+// one wave iteration, at most four), and the block's LDS bytes.
+static int down_rows(bool q8, int K, int N, int nt) {
   const int LPR = K / 64, RPI = 64 / LPR;
   const size_t row_bytes = q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
-  const size_t x_bytes = size_t(nt) * (8 * parts + 2) * LPR * 16;
-  const size_t budget = 60 * 1024 > x_bytes + 4096 ? 60 * 1024 - x_bytes : 4096;
-  const size_t per_iter = size_t(gateup ? 2 : 1) * 4 * RPI * row_bytes;
-  const int iters = int(std::max<size_t>(1, std::min<size_t>(4, budget / per_iter)));
+  const size_t x_bytes = size_t(nt) * xgroups<2>() * LPR * 16;
+  const size_t budget = 44 * 1024 > x_bytes + 4096 ? 44 * 1024 - x_bytes : 4096;
+  const int iters = int(std::max<size_t>(1, std::min<size_t>(4, budget / (4 * RPI * row_bytes))));
   return std::min(N, 4 * RPI * iters);
 }
+static size_t down_smem(bool q8, int K, int rows, int nt) {
+  const size_t row_bytes = q8 ? size_t(K) / 32 * 34 : size_t(K) * 84 / 256;
+  return ((size_t(rows) * row_bytes + 16 + 15) & ~size_t(15)) + size_t(nt) * xgroups<2>() * (K / 64) * 16;
+}
 
-// One GEMV launch (gate/up or down) over `nshared` shared-expert chunks and
-// u_max routed job slots; raises the kernel's LDS limit when needed.
-template <bool GATEUP, int NT, bool XF32>
-static hipError_t launch_gemv(FfnArgs a, bool with_routed, hipStream_t stream) {
-  constexpr int PARTS = GATEUP ? (XF32 ? 2 : 1) : 2;
-  const int K = GATEUP ? a.D : a.F, N = GATEUP ? a.F : a.D;
-  const bool has_shared = GATEUP ? a.sg != nullptr : a.sd != nullptr;
-  const int rows_rt = gemv_rows(GATEUP, false, K, N, NT, PARTS);
-  const int rows_sh = gemv_rows(GATEUP, true, K, N, NT, PARTS);
-  const int chunks_rt = (N + rows_rt - 1) / rows_rt, chunks_sh = has_shared ? (N + rows_sh - 1) / rows_sh : 0;
-  if (GATEUP) {
-    a.rows_gu = rows_rt;
-    a.chunks_gu = chunks_rt;
-    a.rows_sg = rows_sh;
-    a.chunks_sg = chunks_sh;
-  } else {
-    a.rows_dn = rows_rt;
-    a.chunks_dn = chunks_rt;
-    a.rows_sd = rows_sh;
-    a.chunks_sd = chunks_sh;
-  }
-  if (!with_routed) a.u_max = 0;
-  const size_t smem = std::max(with_routed ? gemv_smem(GATEUP, false, K, rows_rt, NT, PARTS) : 0,
-                               has_shared ? gemv_smem(GATEUP, true, K, rows_sh, NT, PARTS) : 0);
-  const unsigned grid = unsigned(chunks_sh + a.u_max * chunks_rt);
+// Gate/up GEMV launch over the shared expert's row chunks and u_max routed
+// job slots: routed blocks hold 4 row iterations per wave, shared (Q8_0, 3.2x
+// the bytes per row) blocks 2.
+template <int NT, bool XF32>
+static hipError_t launch_gateup_gemv(FfnArgs a, hipStream_t stream) {
+  const int rpi = 64 / (a.D / 64);
+  a.rows_gu = min(a.F, 16 * rpi);
+  a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
+  a.rows_sg = min(a.F, 8 * rpi);
+  a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
+  const unsigned grid = unsigned(a.chunks_sg + a.u_max * a.chunks_gu);
+  if (grid == 0) return hipSuccess;
+  BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Down GEMV launch over the shared expert's row chunks and u_max routed job
+// slots; raises the kernel's LDS limit when needed.
+template <int NT>
+static hipError_t launch_down_gemv(FfnArgs a, hipStream_t stream) {
+  a.rows_dn = down_rows(false, a.F, a.D, NT);
+  a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
+  a.rows_sd = down_rows(true, a.F, a.D, NT);
+  a.chunks_sd = a.sd ? (a.D + a.rows_sd - 1) / a.rows_sd : 0;
+  const size_t smem = std::max(a.u_max ? down_smem(false, a.F, a.rows_dn, NT) : 0,
+                               a.sd ? down_smem(true, a.F, a.rows_sd, NT) : 0);
+  const unsigned grid = unsigned(a.chunks_sd + a.u_max * a.chunks_dn);
   if (grid == 0) return hipSuccess;
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_gemv_kernel<GATEUP, NT, XF32>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_down_kernel<NT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
   }
-  BM_LAUNCH(GATEUP ? "ffn_gateup_kernel" : "ffn_down_kernel", (ffn_gemv_kernel<GATEUP, NT, XF32>), dim3(grid),
-            dim3(256), smem, stream, a);
+  BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT>), dim3(grid), dim3(256), smem, stream, a);
   return hipGetLastError();
 }
 
@@ -693,6 +996,8 @@ static size_t mfma_decode_smem(int K, int np, int parts) {
 template <int NT, bool XF32>
 static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
   const size_t cap = 56 * 1024;
+  FfnArgs sh = a;
+  sh.u_max = 0;  // shared row chunks only
   hipError_t err;
   {  // gate/up
     const int parts = XF32 ? 2 : 1;
@@ -702,7 +1007,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
     BM_LAUNCH("ffn_mfma_gateup_kernel", (ffn_mfma_decode_kernel<true, XF32>), dim3(a.u_max * (a.F / 16)), dim3(256),
               mfma_decode_smem(a.D, c.np, parts), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sg && (err = launch_gemv<true, NT, XF32>(a, false, stream)) != hipSuccess) return err;
+    if (a.sg && (err = launch_gateup_gemv<NT, XF32>(sh, stream)) != hipSuccess) return err;
   }
   {  // down
     const size_t per_row = size_t(2) * a.F * 2 + size_t(a.F / 256) * 64;
@@ -711,7 +1016,7 @@ static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
     BM_LAUNCH("ffn_mfma_down_kernel", (ffn_mfma_decode_kernel<false, XF32>), dim3(a.u_max * (a.D / 16)), dim3(256),
               mfma_decode_smem(a.F, c.np, 2), stream, a, c);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sd && (err = launch_gemv<false, (NT > 2 ? 2 : NT), false>(a, false, stream)) != hipSuccess) return err;
+    if (a.sd && (err = launch_down_gemv<(NT > 2 ? 2 : NT)>(sh, stream)) != hipSuccess) return err;
   }
   return hipSuccess;
 }
@@ -761,9 +1066,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 
 template <int NT_GU, int NT_DN, bool XF32>
 static hipError_t launch_decode_nt(const FfnArgs &a, hipStream_t stream) {
-  hipError_t err = launch_gemv<true, NT_GU, XF32>(a, true, stream);
+  hipError_t err = launch_gateup_gemv<NT_GU, XF32>(a, stream);
   if (err != hipSuccess) return err;
-  return launch_gemv<false, NT_DN, false>(a, true, stream);
+  return launch_down_gemv<NT_DN>(a, stream);
 }
 
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
