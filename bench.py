@@ -250,7 +250,10 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
     step_ms = eager_ms / K
     routed = 2.0 * T * k * 3 * D * F
     shared = 2.0 * T * 3 * D * F
-    gemm_ms = prof.get("grouped_gemm_kernel", (0.0, 1))[0] / K
+    # useful FLOP per launch of each expert GEMM
+    gemm_flops = {"routed_gateup_gemm_kernel": 2.0 * T * k * 2 * D * F, "routed_down_gemm_kernel": 2.0 * T * k * D * F,
+                  "shared_gateup_gemm_kernel": 2.0 * T * 2 * D * F, "shared_down_gemm_kernel": 2.0 * T * D * F}
+    gemm_ms = sum(prof.get(n, (0.0, 1))[0] for n in gemm_flops) / K
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.n_experts)
     return {"workload": "prefill chunk T=4096 through one layer (384 experts top-6, Zipf(1.1) router bias "
                         "lambda=0.3, Q8_0 shared expert)",
@@ -259,7 +262,7 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
             "tflops_grouped_gemm": round((routed + shared) / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
             "mfma_bf16_peak_tflops": 2500.0,
             "expert_tokens": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
-            "kernels": kernel_table(prof, {})}
+            "kernels": kernel_table(prof, {}, gemm_flops)}
 
 
 def main() -> int:

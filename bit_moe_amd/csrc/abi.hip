@@ -83,7 +83,7 @@ struct DecodeWs {
 
 struct PrefillWs {
   bm::PlanBufs plan;
-  int32_t *tile_off;
+  int32_t *tile_off, *tile_off2;
   uint16_t *xs, *h, *hs, *h_lo, *hs_lo, *sw;
   float *y, *ys;
 };
@@ -116,7 +116,9 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   w->plan.n_union = static_cast<int32_t *>(c.take(4));
   w->plan.chunk_counts = static_cast<int32_t *>(c.take(bm::plan_scratch_bytes(T, E)));
   w->tile_off = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  w->tile_off2 = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
   w->plan.tile_off = w->tile_off;
+  w->plan.tile_off2 = w->tile_off2;
   w->xs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_model * 2));
   w->h = static_cast<uint16_t *>(c.take(P * L->d_ff * 2));
   w->hs = static_cast<uint16_t *>(c.take(size_t(T) * L->d_ff * 2));
@@ -283,6 +285,7 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   a.plan = w.plan;
   a.plan.status = status;
   a.tile_off = w.tile_off;
+  a.tile_off2 = w.tile_off2;
   a.xs = w.xs;
   a.h = w.h;
   a.hs = w.hs;
@@ -334,8 +337,8 @@ int moe_plan(const int32_t *topk_ids, int32_t T, int32_t k, int32_t n_experts, i
   if (T > 0 && (!topk_ids || !perm)) return fail(BITMOE_EINVAL, "%s: NULL ids or perm", fn);
   size_t need = up256(bm::plan_scratch_bytes(T, n_experts));
   if (!ws || ws_bytes < need) return fail(BITMOE_EWORKSPACE, "%s: workspace %zu bytes, needs %zu", fn, ws_bytes, need);
-  bm::PlanBufs p{counts, offsets, perm, union_ids, n_union, static_cast<int32_t *>(ws), nullptr, status};
-  hipError_t e = bm::launch_plan(topk_ids, T, k, n_experts, 0, p, stream);
+  bm::PlanBufs p{counts, offsets, perm, union_ids, n_union, static_cast<int32_t *>(ws), nullptr, nullptr, status};
+  hipError_t e = bm::launch_plan(topk_ids, T, k, n_experts, 0, 0, p, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }

@@ -35,10 +35,12 @@ struct PlanBufs {
   int32_t *union_ids;
   int32_t *n_union;
   int32_t *chunk_counts;
-  int32_t *tile_off;
+  int32_t *tile_off;   // [E+1] prefix of ceil(count / bm_tile), or null
+  int32_t *tile_off2;  // [E+1] prefix of ceil(count / bm_tile2), or null
   int64_t *status;
 };
-hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, PlanBufs p, hipStream_t stream);
+hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, int bm_tile2, PlanBufs p,
+                       hipStream_t stream);
 size_t plan_scratch_bytes(int T, int E);
 
 struct FfnArgs {
@@ -76,7 +78,8 @@ struct PrefillArgs {
   const int32_t *ids;
   const float *wts;
   PlanBufs plan;
-  int32_t *tile_off;   // [E+1] M-tiles per expert, prefix
+  int32_t *tile_off;   // [E+1] M-tiles of PREFILL_BM tokens per expert, prefix
+  int32_t *tile_off2;  // [E+1] M-tiles of PREFILL_BM_DOWN pairs per expert, prefix
   uint16_t *xs;        // [T][D] bf16 copy of x (x_f32 only)
   uint16_t *h;         // [T*k][F] bf16 hi part of h, pair order
   uint16_t *hs;        // [T][F] bf16 hi part (shared expert)
@@ -90,6 +93,7 @@ struct PrefillArgs {
   int64_t *status;
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
-constexpr int PREFILL_BM = 64;  // tokens per M-tile of the grouped GEMM
+constexpr int PREFILL_BM = 64;       // tokens per M-tile of the gate/up grouped GEMM
+constexpr int PREFILL_BM_DOWN = 32;  // pairs per M-tile of the down grouped GEMM
 
 }  // namespace bm

@@ -42,10 +42,11 @@ __global__ void __launch_bounds__(64) plan_count_kernel(const int32_t *__restric
 }
 
 // One block of 1024 threads.  Thread e owns expert e (E <= 1024).
-__global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, int bm_tile, PlanBufs p) {
+__global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, int bm_tile, int bm_tile2, PlanBufs p) {
   __shared__ int32_t s_cnt[1024];
   __shared__ int32_t s_flag[1024];
   __shared__ int32_t s_tiles[1024];
+  __shared__ int32_t s_tiles2[1024];
   const int e = threadIdx.x;
   int32_t total = 0;
   if (e < E) {
@@ -59,19 +60,22 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, in
   s_cnt[e] = e < E ? total : 0;
   s_flag[e] = (e < E && total > 0) ? 1 : 0;
   s_tiles[e] = (e < E && bm_tile > 0) ? (total + bm_tile - 1) / bm_tile : 0;
+  s_tiles2[e] = (e < E && bm_tile2 > 0) ? (total + bm_tile2 - 1) / bm_tile2 : 0;
   __syncthreads();
   // Hillis-Steele inclusive scans over 1024 entries
   for (int o = 1; o < 1024; o <<= 1) {
-    int32_t a = 0, b = 0, c = 0;
+    int32_t a = 0, b = 0, c = 0, d = 0;
     if (e >= o) {
       a = s_cnt[e - o];
       b = s_flag[e - o];
       c = s_tiles[e - o];
+      d = s_tiles2[e - o];
     }
     __syncthreads();
     s_cnt[e] += a;
     s_flag[e] += b;
     s_tiles[e] += c;
+    s_tiles2[e] += d;
     __syncthreads();
   }
   if (e < E) {
@@ -82,6 +86,10 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, in
     if (p.tile_off) {
       p.tile_off[e + 1] = s_tiles[e];
       if (e == 0) p.tile_off[0] = 0;
+    }
+    if (p.tile_off2) {
+      p.tile_off2[e + 1] = s_tiles2[e];
+      if (e == 0) p.tile_off2[0] = 0;
     }
     if (e == E - 1) *p.n_union = s_flag[e];
   }
@@ -108,13 +116,14 @@ __global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restr
   }
 }
 
-hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, PlanBufs p, hipStream_t stream) {
+hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, int bm_tile2, PlanBufs p,
+                       hipStream_t stream) {
   const int n_chunks = (T + 63) / 64;
   BM_LAUNCH("plan_count_kernel", plan_count_kernel, dim3(n_chunks), dim3(64), E * sizeof(int32_t), stream, ids, T, k, E,
                      p.chunk_counts, p.status);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  BM_LAUNCH("plan_scan_kernel", plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, p);
+  BM_LAUNCH("plan_scan_kernel", plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, bm_tile2, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   BM_LAUNCH("plan_scatter_kernel", plan_scatter_kernel, dim3(n_chunks), dim3(64), 64 * k * sizeof(int32_t), stream, ids, T, k,

@@ -37,6 +37,7 @@
 // then share that XCD's L2 for the activation rows.
 #include "common.h"
 #include "internal.h"
+#include "mfma_q2.h"
 
 namespace bm {
 
@@ -77,139 +78,37 @@ struct GemmArgs {
   int m_tiles;                // grid M-tile slots
 };
 
-// four codes (bytes 0..3, each 0..3) -> two bf16 pairs via a 4-entry table
-BM_DEVICE void lookup4(uint32_t codes, uint32_t tlo, uint32_t thi, uint32_t &p01, uint32_t &p23) {
-  const uint32_t lo = __builtin_amdgcn_perm(0u, tlo, codes);
-  const uint32_t hi = __builtin_amdgcn_perm(0u, thi, codes);
-  p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-  p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-}
-
-// bf16 bits of a small non-negative integer (exact)
-BM_DEVICE uint32_t bf16_of_small(uint32_t v) { return __float_as_uint(float(v)) >> 16; }
-
-// Q2 step operands of one lane for one weight row's super-block:
-//   Bm[t]: exact bf16 sc*q for MFMA step t; Bn: exact bf16 m for the min MFMA;
-//   d, dmin.  `tab` holds per scale value sc the table (tlo, thi) of sc*q.
-BM_DEVICE void q2_operands(const uint8_t *sb, int g, const uint2 *tab, uint32_t (&Bm)[8][4], uint32_t (&Bn)[4],
-                           float &d, float &dmin) {
-  const int h = g >> 1, p = g & 1;
-  const u32x4 q = *reinterpret_cast<const u32x4_a4 *>(sb + 16 + 32 * h + 16 * p);
-  const u32x2 sc = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * h);
-  const u32x2 mn = *reinterpret_cast<const u32x2_a4 *>(sb + 8 * p);
-  const uint32_t dd = *reinterpret_cast<const uint32_t *>(sb + 80);
-  d = half_to_f32(dd & 0xFFFFu);
-  dmin = half_to_f32(dd >> 16);
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  const uint32_t sw0 = sc.x >> (8 * p), sw1 = sc.y >> (8 * p);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint32_t scv = ((s < 2 ? sw0 : sw1) >> (16 * (s & 1))) & 0xFu;
-    const uint2 t = tab[scv];
-#pragma unroll
-    for (int j8 = 0; j8 < 2; ++j8) {
-      uint32_t *o = Bm[2 * s + j8];
-      lookup4((w[2 * j8] >> (2 * s)) & 0x03030303u, t.x, t.y, o[0], o[1]);
-      lookup4((w[2 * j8 + 1] >> (2 * s)) & 0x03030303u, t.x, t.y, o[2], o[3]);
-    }
-  }
-  // min nibbles of sub-blocks 8p .. 8p+7
-  const uint32_t m0 = (mn.x >> 4) & 0x0F0F0F0Fu, m1 = (mn.y >> 4) & 0x0F0F0F0Fu;
-  Bn[0] = bf16_of_small(m0 & 0xFFu) | (bf16_of_small((m0 >> 8) & 0xFFu) << 16);
-  Bn[1] = bf16_of_small((m0 >> 16) & 0xFFu) | (bf16_of_small(m0 >> 24) << 16);
-  Bn[2] = bf16_of_small(m1 & 0xFFu) | (bf16_of_small((m1 >> 8) & 0xFFu) << 16);
-  Bn[3] = bf16_of_small((m1 >> 16) & 0xFFu) | (bf16_of_small(m1 >> 24) << 16);
-}
-
-BM_DEVICE f32x4_t mfma(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4_t c) {
-  u32x4 av = {a[0], a[1], a[2], a[3]};
-  u32x4 bv = {b[0], b[1], b[2], b[3]};
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv),
-                                                 c, 0, 0, 0);
-}
-
-BM_DEVICE void lds_a(const uint16_t *p, uint32_t (&A)[4]) {
-  const uint4 v = *reinterpret_cast<const uint4 *>(p);
-  A[0] = v.x;
-  A[1] = v.y;
-  A[2] = v.z;
-  A[3] = v.w;
-}
-
-// ALO: the A rows arrive as bf16 hi + lo parts (the down projection's h); both
-// parts multiply the same B operand into the same accumulator.
-template <bool GATEUP, int BF, bool ALO>
-__global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs a) {
+// Shared expert (dense, Q8_0 expanded to exact int8 codes as bf16 + one float
+// scale per 32 weights) on MFMA: 64-token M-tiles x 64 weight rows per block,
+// K-steps of 256; each 32-wide MFMA step covers one Q8_0 block, so its result
+// is scaled by d once.  ALO: the A rows arrive as bf16 hi + lo parts (the down
+// projection's h); both parts multiply the same B operand.
+template <bool GATEUP, bool ALO>
+__global__ void __launch_bounds__(256) q8x_gemm_kernel(GemmArgs a) {
   __shared__ uint16_t As[BM_ * LDS_ROW];
   __shared__ uint16_t As_lo[ALO ? BM_ * LDS_ROW : 8];
-  __shared__ uint16_t Xs[BM_ * XS_ROW];
-  __shared__ uint2 tab[16];
   const int nt_n = a.N / BN_;
   // XCD-aware remap of the block index (grid is a multiple of 8)
   const int G = gridDim.x, b = blockIdx.x;
   const int L = (b & 7) * (G >> 3) + (b >> 3);
   const int mt = L / nt_n, ntile = L % nt_n;
   if (mt >= a.m_tiles) return;
-  int e = 0, valid, base;
-  if (a.dense) {
-    const int m0 = mt * BM_;
-    if (m0 >= a.T) return;
-    valid = min(BM_, a.T - m0);
-    base = m0;
-  } else {
-    if (mt >= a.tile_off[a.E]) return;
-    int lo = 0, hi = a.E;  // largest e with tile_off[e] <= mt
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.tile_off[mid] <= mt) lo = mid; else hi = mid;
-    }
-    e = lo;
-    const int m0 = (mt - a.tile_off[e]) * BM_;
-    valid = min(BM_, a.counts[e] - m0);
-    base = a.offsets[e] + m0;
-  }
+  const int base = mt * BM_;
+  if (base >= a.T) return;
+  const int valid = min(BM_, a.T - base);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, nl = lane & 15;
   const int n = ntile * BN_ + wave * 16 + nl;  // this lane's weight row
-  if (BF == BF_Q2 && tid < 16) {
-    // table of bf16(sc*q), q = 0..3, for scale sc = tid: low bytes, high bytes
-    uint32_t lo = 0, hi = 0;
-    for (int q = 1; q < 4; ++q) {
-      const uint32_t v = bf16_of_small(uint32_t(tid * q));
-      lo |= (v & 0xFFu) << (8 * q);
-      hi |= (v >> 8) << (8 * q);
-    }
-    tab[tid] = make_uint2(lo, hi);
-  }
   // A staging slice of this thread: row ar, 64 elements at 64*aq
   const int ar = tid >> 2, aq = tid & 3;
-  int a_row = -1;
-  if (ar < valid) {
-    if (a.dense) {
-      a_row = base + ar;
-    } else {
-      const int pr = a.perm[base + ar];
-      a_row = a.a_by_pair ? pr : pr / a.k;
-    }
-  }
+  const int a_row = ar < valid ? base + ar : -1;
   const uint16_t *a_src = a_row >= 0 ? a.a + size_t(a_row) * a.K : nullptr;
   const uint16_t *a_src_lo = (ALO && a_row >= 0) ? a.a_lo + size_t(a_row) * a.K : nullptr;
-  size_t row_bytes, b_off;
-  if (BF == BF_Q2) {
-    row_bytes = size_t(a.K) / 256 * 84;
-    b_off = size_t(e) * a.b_expert_stride + size_t(n) * row_bytes;
-  } else {
-    row_bytes = size_t(a.K) * 2;
-    b_off = size_t(n) * row_bytes;
-  }
-
+  const size_t b_off = size_t(n) * a.K * 2;
   f32x4_t acc0[4], acc1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc0[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc1[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc0[i] = acc1[i] = zero;
   const int nsteps = a.K / KS;
   for (int kb = 0; kb < nsteps; ++kb) {
     uint4 av[8], al[ALO ? 8 : 1];
@@ -229,101 +128,37 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&As_lo[ar * LDS_ROW + aq * 64 + 8 * i]) = al[i];
     }
-    if (BF == BF_Q2) {
-      // sub-block sums (16 values each) of this slice, split into bf16 hi + lo
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float s = 0.f;
-        const uint4 u0 = av[2 * j], u1 = av[2 * j + 1];
-        const uint32_t w8[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += bf16_lo(w8[i]) + bf16_hi(w8[i]);
-        if constexpr (ALO) {
-          const uint4 l0 = al[2 * j], l1 = al[2 * j + 1];
-          const uint32_t v8[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s += bf16_lo(v8[i]) + bf16_hi(v8[i]);
-        }
-        const uint16_t shi = f32_to_bf16(s);
-        Xs[ar * XS_ROW + 4 * aq + j] = shi;
-        Xs[ar * XS_ROW + 16 + 4 * aq + j] = f32_to_bf16(s - bf16_to_f32(shi));
-      }
-    }
     __syncthreads();
-    if constexpr (BF == BF_Q2) {
-      const int h = g >> 1, p = g & 1;
-      uint32_t Bm0[8][4], Bn0[4], Bm1[8][4], Bn1[4];
-      float d0, dm0, d1 = 0.f, dm1 = 0.f;
-      q2_operands(a.b0 + b_off + size_t(kb) * 84, g, tab, Bm0, Bn0, d0, dm0);
-      if constexpr (GATEUP) q2_operands(a.b1 + b_off + size_t(kb) * 84, g, tab, Bm1, Bn1, d1, dm1);
-      f32x4_t cm0[4], cm1[4], cn0[4], cn1[4];
+    const uint16_t *r0 = reinterpret_cast<const uint16_t *>(a.b0 + b_off) + kb * KS;
+    const uint16_t *r1 = GATEUP ? reinterpret_cast<const uint16_t *>(a.b1 + b_off) + kb * KS : nullptr;
+    const float *s0 = a.d0 + size_t(n) * (a.K / 32) + kb * 8;
+    const float *s1 = GATEUP ? a.d1 + size_t(n) * (a.K / 32) + kb * 8 : nullptr;
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) cm0[mi] = cm1[mi] = zero;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int ko = 128 * h + 32 * (t >> 1) + 16 * p + 8 * (t & 1);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          uint32_t A[4];
-          lds_a(&As[(16 * mi + nl) * LDS_ROW + ko], A);
-          cm0[mi] = mfma(A, Bm0[t], cm0[mi]);
-          if constexpr (GATEUP) cm1[mi] = mfma(A, Bm1[t], cm1[mi]);
-          if constexpr (ALO) {
-            lds_a(&As_lo[(16 * mi + nl) * LDS_ROW + ko], A);
-            cm0[mi] = mfma(A, Bm0[t], cm0[mi]);
-          }
-        }
+    for (int t = 0; t < 8; ++t) {
+      uint32_t B0[4], B1[4];
+      ld16(r0 + 32 * t + 8 * g, B0);
+      const float e0 = s0[t];
+      float e1 = 0.f;
+      if constexpr (GATEUP) {
+        ld16(r1 + 32 * t + 8 * g, B1);
+        e1 = s1[t];
       }
-      // min term: k-slot (g, i) = part g/2 (hi, lo) of sub-block sum 8p + i
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
         uint32_t A[4];
-        lds_a(&Xs[(16 * mi + nl) * XS_ROW + 16 * (g >> 1) + 8 * p], A);
-        cn0[mi] = mfma(A, Bn0, zero);
-        if constexpr (GATEUP) cn1[mi] = mfma(A, Bn1, zero);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc0[mi][r] = __builtin_fmaf(d0, cm0[mi][r], __builtin_fmaf(-dm0, cn0[mi][r], acc0[mi][r]));
-          if constexpr (GATEUP)
-            acc1[mi][r] = __builtin_fmaf(d1, cm1[mi][r], __builtin_fmaf(-dm1, cn1[mi][r], acc1[mi][r]));
+        ld16(&As[(16 * mi + nl) * LDS_ROW + 32 * t + 8 * g], A);
+        f32x4_t c0 = mfma16(A, B0, zero);
+        if constexpr (ALO) {
+          uint32_t Alo[4];
+          ld16(&As_lo[(16 * mi + nl) * LDS_ROW + 32 * t + 8 * g], Alo);
+          c0 = mfma16(Alo, B0, c0);
         }
-      }
-    } else {
-      // expanded Q8_0: exact int8 codes as bf16, one float d per 32 weights
-      const uint16_t *r0 = reinterpret_cast<const uint16_t *>(a.b0 + b_off) + kb * KS;
-      const uint16_t *r1 = GATEUP ? reinterpret_cast<const uint16_t *>(a.b1 + b_off) + kb * KS : nullptr;
-      const float *s0 = a.d0 + size_t(n) * (a.K / 32) + kb * 8;
-      const float *s1 = GATEUP ? a.d1 + size_t(n) * (a.K / 32) + kb * 8 : nullptr;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        uint32_t B0[4], B1[4];
-        lds_a(r0 + 32 * t + 8 * g, B0);
-        const float e0 = s0[t];
-        float e1 = 0.f;
+        for (int r = 0; r < 4; ++r) acc0[mi][r] = __builtin_fmaf(e0, c0[r], acc0[mi][r]);
         if constexpr (GATEUP) {
-          lds_a(r1 + 32 * t + 8 * g, B1);
-          e1 = s1[t];
-        }
+          const f32x4_t c1 = mfma16(A, B1, zero);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          uint32_t A[4];
-          lds_a(&As[(16 * mi + nl) * LDS_ROW + 32 * t + 8 * g], A);
-          f32x4_t c0 = mfma(A, B0, zero);
-          if constexpr (ALO) {
-            uint32_t Al[4];
-            lds_a(&As_lo[(16 * mi + nl) * LDS_ROW + 32 * t + 8 * g], Al);
-            c0 = mfma(Al, B0, c0);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc0[mi][r] = __builtin_fmaf(e0, c0[r], acc0[mi][r]);
-          if constexpr (GATEUP) {
-            const f32x4_t c1 = mfma(A, B1, zero);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc1[mi][r] = __builtin_fmaf(e1, c1[r], acc1[mi][r]);
-          }
+          for (int r = 0; r < 4; ++r) acc1[mi][r] = __builtin_fmaf(e1, c1[r], acc1[mi][r]);
         }
       }
     }
@@ -335,17 +170,227 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int m = 16 * mi + 4 * g + r;
       if (m >= valid) continue;
-      const int orow = a.dense ? base + m : a.perm[base + m];
+      const size_t orow = size_t(base + m);
       if constexpr (GATEUP) {
         const float hf = silu(acc0[mi][r]) * acc1[mi][r];
         const uint16_t hb = f32_to_bf16(hf);
-        a.h_out[size_t(orow) * a.N + n] = hb;
-        a.h_lo_out[size_t(orow) * a.N + n] = f32_to_bf16(hf - bf16_to_f32(hb));
+        a.h_out[orow * a.N + n] = hb;
+        a.h_lo_out[orow * a.N + n] = f32_to_bf16(hf - bf16_to_f32(hb));
       } else {
-        a.y_out[size_t(orow) * a.N + n] = acc0[mi][r];
+        a.y_out[orow * a.N + n] = acc0[mi][r];
       }
     }
   }
+}
+
+// ---- routed Q2 grouped GEMM with asynchronous activation staging ---------------
+// Block tile: BMt = 16 MI rows (tokens or pairs of one expert) x BNt = 4 waves x
+// 16 NG weight rows; K-steps of one super-block (256).  While step kb
+// computes, the BMt activation rows of step kb+1 (and their lo parts for the
+// down projection) are copied into the other half of a double LDS buffer with
+// direct-to-LDS loads (one 512-byte row per instruction), and each lane's
+// weight bytes of kb+1 are loaded into registers; the block waits for both
+// once per step.  The sub-block sums of the step's rows are formed from LDS.
+// Per wave and step: 8 x MI x NG x NM main MFMAs (+ the lo parts) on exact
+// B = bf16(sc*q), and MI x NG x NM min MFMAs against the sums.
+template <bool GATEUP, int MI, int NG, bool ALO>
+__global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
+  constexpr int BMt = 16 * MI, BNt = 64 * NG, PARTS = ALO ? 2 : 1, NM = GATEUP ? 2 : 1;
+  constexpr int ROWB = LDS_ROW * 2;        // bytes per LDS activation row
+  constexpr int BUF = PARTS * BMt * ROWB;  // bytes per buffer half
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_q2[];
+  uint16_t *Xs = reinterpret_cast<uint16_t *>(smem_q2 + 2 * BUF);  // [BMt][XS_ROW]
+  uint2 *tab = reinterpret_cast<uint2 *>(Xs + BMt * XS_ROW);       // [16]
+  int32_t *rows = reinterpret_cast<int32_t *>(tab + 16);           // [BMt] activation row, -1: none
+  const int nt_n = a.N / BNt;
+  // XCD-aware remap of the block index (grid is a multiple of 8)
+  const int G = gridDim.x, b = blockIdx.x;
+  const int L = (b & 7) * (G >> 3) + (b >> 3);
+  const int mt = L / nt_n, ntile = L % nt_n;
+  if (mt >= a.m_tiles || mt >= a.tile_off[a.E]) return;
+  int lo = 0, hi = a.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_off[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int m0 = (mt - a.tile_off[e]) * BMt;
+  const int valid = min(BMt, a.counts[e] - m0);
+  const int base = a.offsets[e] + m0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, nl = lane & 15, p = g & 1;
+  if (tid < 16) tab[tid] = sc_table_entry(tid);
+  for (int i = tid; i < BMt; i += 256) {
+    int r = -1;
+    if (i < valid) {
+      const int pr = a.perm[base + i];
+      r = a.a_by_pair ? pr : pr / a.k;
+    }
+    rows[i] = r;
+  }
+  __syncthreads();
+  const size_t row_bytes = size_t(a.K) / 256 * 84;
+  const uint8_t *wb[2] = {a.b0 + size_t(e) * a.b_expert_stride, NM > 1 ? a.b1 + size_t(e) * a.b_expert_stride : nullptr};
+  const int n_w = ntile * BNt + wave * 16 * NG + nl;  // weight row of group 0; group ng adds 16 ng
+  auto issue_a = [&](int kb, int half) {
+    uint8_t *dst = smem_q2 + half * BUF;
+    for (int i = wave; i < PARTS * BMt; i += 4) {
+      const int part = i / BMt, r = i % BMt;
+      const int src_row = rows[r];
+      if (src_row >= 0 && lane < 32) {
+        const uint16_t *src = (part ? a.a_lo : a.a) + size_t(src_row) * a.K + kb * KS + 8 * lane;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
+                                         (__attribute__((address_space(3))) void *)(dst + (part * BMt + r) * ROWB),
+                                         16, 0, 0);
+      }
+    }
+  };
+  auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) raw[ng][m] = q2_load(wb[m] + size_t(n_w + 16 * ng) * row_bytes + size_t(kb) * 84, g);
+  };
+  f32x4_t acc[MI][NG][NM];
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[mi][ng][m] = zero;
+  Q2Raw cur[NG][NM];
+  issue_a(0, 0);
+  load_b(0, cur);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const int nsteps = a.K / KS;
+  for (int kb = 0; kb < nsteps; ++kb) {
+    Q2Raw nxt[NG][NM];
+    if (kb + 1 < nsteps) {
+      issue_a(kb + 1, (kb + 1) & 1);
+      load_b(kb + 1, nxt);
+    }
+    const uint8_t *cb = smem_q2 + (kb & 1) * BUF;
+    // sub-block sums of the step's rows (all parts), split into bf16 hi + lo
+    for (int idx = tid; idx < BMt * 16; idx += 256) {
+      const int r = idx >> 4, sb = idx & 15;
+      float sum = 0.f;
+#pragma unroll
+      for (int part = 0; part < PARTS; ++part) {
+        const uint4 *v = reinterpret_cast<const uint4 *>(cb + (part * BMt + r) * ROWB + sb * 32);
+        const uint4 v0 = v[0], v1 = v[1];
+        const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sum += bf16_lo(w8[i]) + bf16_hi(w8[i]);
+      }
+      const uint16_t shi = f32_to_bf16(sum);
+      Xs[r * XS_ROW + q2_sum_slot(sb, 0)] = shi;
+      Xs[r * XS_ROW + q2_sum_slot(sb, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
+    }
+    __syncthreads();
+    f32x4_t cm[MI][NG][NM];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) cm[mi][ng][m] = zero;
+    const uint16_t *Ah = reinterpret_cast<const uint16_t *>(cb);
+    const uint16_t *Al = reinterpret_cast<const uint16_t *>(cb + BMt * ROWB);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int ko = q2_kofs(t, g);
+      uint32_t B[NG][NM][4];
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) q2_main_operand(cur[ng][m], p, t, tab, B[ng][m]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        uint32_t A[4];
+        ld16(Ah + (16 * mi + nl) * LDS_ROW + ko, A);
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) cm[mi][ng][m] = mfma16(A, B[ng][m], cm[mi][ng][m]);
+        if constexpr (ALO) {
+          ld16(Al + (16 * mi + nl) * LDS_ROW + ko, A);
+#pragma unroll
+          for (int ng = 0; ng < NG; ++ng) cm[mi][ng][0] = mfma16(A, B[ng][0], cm[mi][ng][0]);
+        }
+      }
+    }
+    // min term against the sums, then d and dmin of the super-block
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        uint32_t Bn[4];
+        q2_min_operand(cur[ng][m], p, Bn);
+        const float d = q2_d(cur[ng][m]), dm = q2_dmin(cur[ng][m]);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          uint32_t As[4];
+          ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As);
+          const f32x4_t cn = mfma16(As, Bn, zero);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[mi][ng][m][r] = __builtin_fmaf(d, cm[mi][ng][m][r], __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
+        }
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows and weight bytes have landed
+    __syncthreads();  // ... and this step's buffer half and sums are no longer read
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) cur[ng][m] = nxt[ng][m];
+  }
+  // epilogue: lane holds rows 16 mi + 4 g + r of column n_w + 16 ng
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mrow = 16 * mi + 4 * g + r;
+      if (mrow >= valid) continue;
+      const size_t orow = size_t(a.perm[base + mrow]);
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        const int n = n_w + 16 * ng;
+        if constexpr (GATEUP) {
+          const float hf = silu(acc[mi][ng][0][r]) * acc[mi][ng][NM - 1][r];
+          const uint16_t hb = f32_to_bf16(hf);
+          a.h_out[orow * a.N + n] = hb;
+          a.h_lo_out[orow * a.N + n] = f32_to_bf16(hf - bf16_to_f32(hb));
+        } else {
+          a.y_out[orow * a.N + n] = acc[mi][ng][0][r];
+        }
+      }
+    }
+  }
+}
+
+template <bool GATEUP, int MI, int NG, bool ALO>
+static size_t q2_gemm_smem() {
+  return size_t(2) * (ALO ? 2 : 1) * 16 * MI * LDS_ROW * 2 + size_t(16) * MI * XS_ROW * 2 + 16 * 8 + size_t(16) * MI * 4;
+}
+
+template <bool GATEUP, int MI, int NG, bool ALO>
+static hipError_t launch_q2_gemm(const GemmArgs &g, hipStream_t stream) {
+  const size_t smem = q2_gemm_smem<GATEUP, MI, NG, ALO>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q2_gemm_kernel<GATEUP, MI, NG, ALO>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int grid = g.m_tiles * (g.N / (64 * NG));
+  grid = (grid + 7) & ~7;
+  BM_LAUNCH(GATEUP ? "routed_gateup_gemm_kernel" : "routed_down_gemm_kernel", (q2_gemm_kernel<GATEUP, MI, NG, ALO>),
+            dim3(grid), dim3(256), smem, stream, g);
+  return hipGetLastError();
 }
 
 // Q8_0 [N][K] -> exact bf16 codes [N][K] and float scales [N][K/32]
@@ -374,17 +419,13 @@ __global__ void __launch_bounds__(256) f32_to_bf16_kernel(const float *__restric
   *reinterpret_cast<uint2 *>(y + i) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-static hipError_t launch_gemm(const GemmArgs &g, bool gateup, bool q2, hipStream_t stream) {
+static hipError_t launch_q8x_gemm(const GemmArgs &g, bool gateup, hipStream_t stream) {
   int grid = g.m_tiles * (g.N / BN_);
   grid = (grid + 7) & ~7;
-  if (gateup && q2)
-    BM_LAUNCH("grouped_gemm_kernel", (grouped_gemm_kernel<true, BF_Q2, false>), dim3(grid), dim3(256), 0, stream, g);
-  else if (gateup)
-    BM_LAUNCH("grouped_gemm_kernel", (grouped_gemm_kernel<true, BF_Q8X, false>), dim3(grid), dim3(256), 0, stream, g);
-  else if (q2)
-    BM_LAUNCH("grouped_gemm_kernel", (grouped_gemm_kernel<false, BF_Q2, true>), dim3(grid), dim3(256), 0, stream, g);
+  if (gateup)
+    BM_LAUNCH("shared_gateup_gemm_kernel", (q8x_gemm_kernel<true, false>), dim3(grid), dim3(256), 0, stream, g);
   else
-    BM_LAUNCH("grouped_gemm_kernel", (grouped_gemm_kernel<false, BF_Q8X, true>), dim3(grid), dim3(256), 0, stream, g);
+    BM_LAUNCH("shared_down_gemm_kernel", (q8x_gemm_kernel<false, true>), dim3(grid), dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -408,9 +449,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
     x = a.xs;
   }
   PlanBufs p = a.plan;
-  if ((err = launch_plan(a.ids, a.T, a.k, a.E, BM_, p, stream)) != hipSuccess) return err;
+  if ((err = launch_plan(a.ids, a.T, a.k, a.E, BM_, PREFILL_BM_DOWN, p, stream)) != hipSuccess) return err;
   const int P = a.T * a.k;
-  const int m_slots = (P + BM_ - 1) / BM_ + min(a.E, P);
   const size_t q2_stride = size_t(a.F) * a.D / 256 * 84;
 
   GemmArgs g{};
@@ -421,9 +461,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.perm = p.perm;
   g.offsets = p.offsets;
   g.counts = p.counts;
-  g.tile_off = p.tile_off;
-  g.m_tiles = m_slots;
-  // routed gate/up: A = x rows by token, N = F
+  // routed gate/up: A = x rows by token, N = F; tiles of 32 tokens x 128 rows
+  g.tile_off = p.tile_off2;
+  g.m_tiles = (P + PREFILL_BM_DOWN - 1) / PREFILL_BM_DOWN + min(a.E, P);
   g.a = x;
   g.a_by_pair = 0;
   g.K = a.D;
@@ -433,8 +473,10 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.b_expert_stride = q2_stride;
   g.h_out = a.h;
   g.h_lo_out = a.h_lo;
-  if ((err = launch_gemm(g, true, true, stream)) != hipSuccess) return err;
-  // routed down: A = h rows (hi + lo) by pair, N = D
+  if ((err = launch_q2_gemm<true, 2, 2, false>(g, stream)) != hipSuccess) return err;
+  // routed down: A = h rows (hi + lo) by pair, N = D; tiles of 32 pairs x 256 rows
+  g.tile_off = p.tile_off2;
+  g.m_tiles = (P + PREFILL_BM_DOWN - 1) / PREFILL_BM_DOWN + min(a.E, P);
   g.a = a.h;
   g.a_lo = a.h_lo;
   g.a_by_pair = 1;
@@ -443,7 +485,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.b0 = a.wd;
   g.b1 = nullptr;
   g.y_out = a.y;
-  if ((err = launch_gemm(g, false, true, stream)) != hipSuccess) return err;
+  if ((err = launch_q2_gemm<false, 2, 4, true>(g, stream)) != hipSuccess) return err;
 
   if (a.sg) {
     // shared expert: expand Q8_0 to exact bf16 codes + float scales, then dense GEMMs
@@ -468,7 +510,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
     s.b_expert_stride = 0;
     s.h_out = a.hs;
     s.h_lo_out = a.hs_lo;
-    if ((err = launch_gemm(s, true, false, stream)) != hipSuccess) return err;
+    if ((err = launch_q8x_gemm(s, true, stream)) != hipSuccess) return err;
     s.a = a.hs;
     s.a_lo = a.hs_lo;
     s.K = a.F;
@@ -478,7 +520,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
     s.d0 = sd + 2 * nw / 32;
     s.d1 = nullptr;
     s.y_out = a.ys;
-    if ((err = launch_gemm(s, false, false, stream)) != hipSuccess) return err;
+    if ((err = launch_q8x_gemm(s, false, stream)) != hipSuccess) return err;
   }
   return launch_combine(a.y, a.sg ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
                         stream);
