@@ -38,7 +38,7 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode T=1/5), TFLOP/s (prefil
 HBM_PEAK_GBPS = 8000.0
 Q2_MAT = 4096 * 2048 // 256 * 84  # 2,752,512 B
 Q8_MAT = 4096 * 2048 // 32 * 34  # 8,912,896 B
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "ffn_gateup_kernel__decode_T1.md")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "ffn_gateup_kernel__decode_T1.txt")
 
 
 def log(msg: str) -> None:
@@ -278,6 +278,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill workloads")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run 3 plain device-to-device copies of MIB MiB (reference kernel for the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of this "
@@ -296,6 +299,15 @@ def main() -> int:
     bm.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB device-to-device copies")
+        del src, dst
     cfg = synthdata.CONFIGS["decode"]
     K, W, NI = args.steps, args.warmup, args.instances
     lut = torch.from_numpy(synthdata.half_normal_lut().view(np.int16).copy()).to(dev)
