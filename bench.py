@@ -45,20 +45,32 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(T: int, U: int, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
-    """Bytes the method must move per kernel launch (decode path)."""
+def algorithmic_bytes(T: int, U: float, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
+    """Bytes the method must move per launch of each decode kernel that runs at
+    T tokens with U distinct experts: at T <= 2 the GEMV kernels hold routed and
+    shared rows, at T >= 3 the routed experts run on the MFMA kernels and the
+    GEMV kernels hold the shared expert only.  h travels as bf16 hi + lo."""
     P = T * k
-    gateup = U * 2 * Q2_MAT + 2 * Q8_MAT + T * D * 2 + (P + T) * F * 2 * 2  # h as bf16 hi + lo
-    down = U * Q2_MAT + Q8_MAT + (P + T) * F * 2 * 2 + (P + T) * D * 4
-    return {
-        "router_gemv_kernel": E * D * 4 + T * D * 2 + T * E * 4,
+    x = T * D * 2
+    h_pairs, h_tok = P * F * 2 * 2, T * F * 2 * 2
+    routed_gu = U * 2 * Q2_MAT + x + h_pairs
+    shared_gu = 2 * Q8_MAT + x + h_tok
+    routed_dn = U * Q2_MAT + h_pairs + P * D * 4
+    shared_dn = Q8_MAT + h_tok + T * D * 4
+    out = {
+        "router_gemv_kernel": E * D * 4 + x + T * E * 4,
         "topk_kernel": T * E * 4 + P * 8,
-        "ffn_gateup_kernel": gateup,
-        "ffn_down_kernel": down,
-        "ffn_mfma_gateup_kernel": gateup,
-        "ffn_mfma_down_kernel": down,
         "combine_kernel": (P + T) * D * 4 + P * 8 + T * D * 2,
     }
+    if T <= 2:
+        out["ffn_gateup_kernel"] = routed_gu + shared_gu - x  # one activation read
+        out["ffn_down_kernel"] = routed_dn + shared_dn
+    else:
+        out["ffn_mfma_gateup_kernel"] = routed_gu
+        out["ffn_gateup_kernel"] = shared_gu
+        out["ffn_mfma_down_kernel"] = routed_dn
+        out["ffn_down_kernel"] = shared_dn
+    return out
 
 
 def source_hash(path: str) -> str:
@@ -265,6 +277,92 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
             "kernels": kernel_table(prof, {}, gemm_flops)}
 
 
+def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """40-layer resident stack: decode T=1 and T=5 (HIP graph) and a prefill
+    chunk of T=8192 (eager), each step running every layer (route, experts +
+    combine, Engram at layers 1 and 14, residual step)."""
+    cfg = synthdata.CONFIGS["stack"]
+    t0 = time.time()
+    layers = [make_layer(bm, torch, synthdata, cfg, args.seed, l, lut, dev)[0] for l in range(cfg.n_layers)]
+    tables = {}
+    for j, l in enumerate(cfg.engram_layers):
+        t = torch.empty(synthdata.ENGRAM_ROWS * 264, dtype=torch.uint8, device=dev)
+        bm.fill(t, synthdata.tensor_key(args.seed, synthdata.KIND_ENGRAM, j), bm.FILL_ENGRAM, lut)
+        tables[l] = (t.view(synthdata.ENGRAM_ROWS, 264), j)
+    torch.cuda.synchronize()
+    log(f"[bench] stack: {cfg.n_layers} layers resident ({time.time() - t0:.1f} s)")
+    D, F, k = cfg.d_model, cfg.d_ff, cfg.top_k
+    out = {"workload": f"{cfg.n_layers}-layer resident stack (384 experts top-6 per layer, Q8_0 shared expert, "
+                       f"Engram at layers {list(cfg.engram_layers)}, residual RMS rescale between layers)"}
+
+    def run_phase(T, K, W, mode, graph):
+        n = K + W
+        xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 60 + T, n * T, D).view(np.int16)).to(dev)
+        xs = xs.view(torch.bfloat16).view(n, T, D)
+        toks = synthdata.token_ids(args.seed, 70 + T, n * (T + cfg.history))
+        rid = []  # per step, per Engram layer j: row ids [T][8] of table j
+        for i in range(n):
+            r = synthdata.engram_row_ids(args.seed, toks[i * (T + cfg.history):(i + 1) * (T + cfg.history)],
+                                         cfg.history)  # [T][2][8]
+            rid.append([torch.from_numpy(np.ascontiguousarray(r[:, j, :])).to(dev) for j in range(2)])
+        ws = bm.workspace(layers[0], T, mode)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+        xb = [torch.empty((T, D), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        rows = torch.empty((T, 8, 256), dtype=torch.int16, device=dev)
+
+        def step(i):
+            x = xs[i]
+            for l, L in enumerate(layers):
+                bm.route(L, x, ws, ids=ids, weights=wts)
+                bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=mode)
+                if l in tables:
+                    t, j = tables[l]
+                    bm.engram_gather(t, rid[i][j], out=rows)
+                x = bm.residual_rescale(x, y, out=xb[l & 1])
+
+        graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, graph)
+        step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
+        del ws
+        return step_ms, eager_ms / K, prof
+
+    # decode phases
+    for T, K in ((1, 50), (5, 20)):
+        step_ms, eager_ms, prof = run_phase(T, K, 5, bm.MODE_DECODE, not args.no_graph)
+        # union per layer (routing of step 0's input through the stack, outside the timed region)
+        per_layer = 0.0
+        x = torch.from_numpy(synthdata.activations_bf16(args.seed, 60 + T, T, D).view(np.int16)).to(dev)
+        x = x.view(torch.bfloat16).view(T, D)
+        ws = bm.workspace(layers[0], T)
+        U = []
+        for L in layers:
+            ids, w = bm.route(L, x, ws)
+            U.append(len(np.unique(ids.cpu().numpy())))
+            y = bm.expert_ffn(L, x, ids, w, ws)
+            x = bm.residual_rescale(x, y)
+        del ws
+        for u in U:
+            per_layer += sum(algorithmic_bytes(T, u).values()) + 3 * T * D * 2  # + residual step
+        eng = len(cfg.engram_layers) * (T * 8 * (264 + 512) + T * 8 * 8)
+        total = per_layer + eng
+        out[f"decode_T{T}"] = {"tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 4),
+                               "eager_ms_per_step": round(eager_ms, 4), "union_mean": round(float(np.mean(U)), 2),
+                               "algorithmic_bytes_per_step": int(total),
+                               "hbm_gbps": round(total / (step_ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] stack decode T={T}: {step_ms * 1000:.1f} us/step")
+    # prefill phase
+    T = cfg.prefill_T
+    step_ms, _, prof = run_phase(T, args.stack_prefill_steps, 1, bm.MODE_PREFILL, False)
+    flops = cfg.n_layers * (2.0 * T * k * 3 * D * F + 2.0 * T * 3 * D * F)
+    out[f"prefill_T{T}"] = {"tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 3),
+                            "tflops": round(flops / (step_ms * 1e-3) / 1e12, 1)}
+    log(f"[bench] stack prefill T={T}: {step_ms:.1f} ms/step")
+    del layers, tables
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,7 +375,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the verify and prefill workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip the verify, prefill and stack workloads")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack workload")
+    ap.add_argument("--stack-prefill-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 plain device-to-device copies of MIB MiB (reference kernel for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -376,6 +476,10 @@ def main() -> int:
         log("[bench] prefill workload")
         out["prefill"] = bench_prefill(bm, torch, np, synthdata, args, lut, dev)
         torch.cuda.empty_cache()
+        if not args.no_stack:
+            log("[bench] 40-layer stack workload")
+            out["stack"] = bench_stack(bm, torch, np, synthdata, args, lut, dev)
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)

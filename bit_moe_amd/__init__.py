@@ -30,6 +30,7 @@ EXPORTS = [
     "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
+    "bitmoe_residual_rescale",
 ]
 
 
@@ -73,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bitmoe_fill": [P, I64, ctypes.c_uint64, I32, P, P],
         "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "bitmoe_probe_read": [P, I64, P, I32, P],
+        "bitmoe_residual_rescale": [P, P, I32, I32, I32, P, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -296,3 +298,20 @@ def profile_stop() -> dict:
 def probe_read(src: torch.Tensor, n_bytes: int, sink: torch.Tensor, blocks: int, stream=None) -> None:
     """Enqueue the streaming-read probe over the first n_bytes of src."""
     _check(load().bitmoe_probe_read(_ptr(src), n_bytes, _ptr(sink), blocks, _stream(stream)))
+
+
+def residual_rescale(x: torch.Tensor, y: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Residual step of a layer stack: out = bf16((x + y) / rms(x + y)) per row; x [T][D] bf16, y [T][D]
+    float32 or bf16; out may be x."""
+    lib = load()
+    _require(x, "x", torch.bfloat16)
+    _require(y, "y")
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("y must be float32 or bfloat16")
+    T, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", torch.bfloat16)
+    _check(lib.bitmoe_residual_rescale(_ptr(x), _ptr(y), F32 if y.dtype == torch.float32 else BF16, T, D, _ptr(out),
+                                       _stream(stream)))
+    return out

@@ -381,6 +381,20 @@ int bitmoe_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, int32_t 
   return BITMOE_OK;
 }
 
+int bitmoe_residual_rescale(const void *x, const void *y, int32_t y_dtype, int32_t T, int32_t D, void *x_out,
+                            hipStream_t stream) {
+  const char *fn = "bitmoe_residual_rescale";
+  if (T < 0 || D < 16 || D > 4096 || D % 16) return fail(BITMOE_EINVAL, "%s: T=%d D=%d unsupported", fn, T, D);
+  if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
+  if (T == 0) return BITMOE_OK;
+  if (!x || !y || !x_out || !aligned(x, 16) || !aligned(y, 16) || !aligned(x_out, 16))
+    return fail(BITMOE_EINVAL, "%s: NULL or misaligned pointer", fn);
+  hipError_t e = bm::launch_residual_rescale(static_cast<const uint16_t *>(x), y, y_dtype == BITMOE_F32, T, D,
+                                             static_cast<uint16_t *>(x_out), stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
 int bitmoe_read_status(const int64_t *status, hipStream_t stream, int64_t *code, int64_t *detail) {
   if (!status || !code || !detail) return fail(BITMOE_EINVAL, "bitmoe_read_status: NULL argument");
   hipError_t e = hipStreamSynchronize(stream);

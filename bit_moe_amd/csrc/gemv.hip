@@ -1034,18 +1034,25 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
   const int t = int(idx / per_tok);
   const int c = int(idx % per_tok) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
+  // the pair rows are loaded together with the ids (every row of y is in
+  // bounds; rows of skipped pairs are never used)
+  float4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) v[j] = *reinterpret_cast<const float4 *>(y + (int64_t(t) * k + j) * D + c);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
     const int e = ids[t * k + j];
     if (e < 0 || e >= E) {
       if (c == 0) record_fault(status, 1, int64_t(t) * k + j);
       continue;
     }
     const float w = wts[t * k + j];
-    const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t(t) * k + j) * D + c);
-    acc.x = __builtin_fmaf(w, v.x, acc.x);
-    acc.y = __builtin_fmaf(w, v.y, acc.y);
-    acc.z = __builtin_fmaf(w, v.z, acc.z);
-    acc.w = __builtin_fmaf(w, v.w, acc.w);
+    acc.x = __builtin_fmaf(w, v[j].x, acc.x);
+    acc.y = __builtin_fmaf(w, v[j].y, acc.y);
+    acc.z = __builtin_fmaf(w, v[j].z, acc.z);
+    acc.w = __builtin_fmaf(w, v[j].w, acc.w);
   }
   if (ys) {
     const float4 v = *reinterpret_cast<const float4 *>(ys + int64_t(t) * D + c);

@@ -93,6 +93,8 @@ struct PrefillArgs {
   int64_t *status;
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,
+                                   hipStream_t stream);
 constexpr int PREFILL_BM = 64;       // tokens per M-tile of the gate/up grouped GEMM
 constexpr int PREFILL_BM_DOWN = 32;  // pairs per M-tile of the down grouped GEMM
 

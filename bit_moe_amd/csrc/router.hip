@@ -141,8 +141,8 @@ BM_DEVICE float key_logit(uint32_t key) {
 // Round j: the wave-wide largest key M (DPP reduction); the selected expert is
 // the lowest index holding M (lowest slot i, then lowest lane, by ballot), so
 // an exact tie goes to the lower expert index.
+template <int PER>  // logits per lane: E <= 64 PER
 BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts, int lane) {
-  constexpr int PER = 16;  // E <= 1024
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -186,11 +186,12 @@ BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts
   }
 }
 
+template <int PER>
 __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ ids, float *__restrict__ wts) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_token(logits + int64_t(t) * E, E, k, ids + int64_t(t) * k, wts + int64_t(t) * k, threadIdx.x & 63);
+  topk_token<PER>(logits + int64_t(t) * E, E, k, ids + int64_t(t) * k, wts + int64_t(t) * k, threadIdx.x & 63);
 }
 
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
@@ -210,7 +211,12 @@ hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, c
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  BM_LAUNCH("topk_kernel", topk_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k, ids, wts);
+  // blocks of 4 waves for T > 1; a single wave for one token
+  const dim3 grid((T + 3) / 4), block(T == 1 ? 64 : 256);
+  if (E <= 6 * 64)
+    BM_LAUNCH("topk_kernel", topk_kernel<6>, grid, block, 0, stream, logits, T, E, k, ids, wts);
+  else
+    BM_LAUNCH("topk_kernel", topk_kernel<16>, grid, block, 0, stream, logits, T, E, k, ids, wts);
   return hipGetLastError();
 }
 

@@ -232,6 +232,9 @@ class Config:
     zipf_lambda: Optional[float] = None
     engram: bool = False
     history: int = 0  # tokens of history before the batch (Engram hashing)
+    n_layers: int = 1  # layers of a resident stack (each with its own seeded tensors)
+    engram_layers: tuple = ()  # stack layers that gather Engram rows (one table each)
+    prefill_T: int = 0  # stack prefill chunk
 
 
 CONFIGS = {
@@ -243,6 +246,9 @@ CONFIGS = {
     "verify": Config("verify", 5, 4096, 2048, 384, 6, "bf16", True, engram=True, history=3),
     # prefill chunk of 4096 tokens with a Zipf(1.1) router bias
     "prefill": Config("prefill", 4096, 4096, 2048, 384, 6, "bf16", True, zipf_lambda=0.3),
+    # 40-layer resident stack: decode T=1 and T=5, prefill 8192; Engram at layers 1 and 14
+    "stack": Config("stack", 1, 4096, 2048, 384, 6, "bf16", True, engram=True, history=3, n_layers=40,
+                    engram_layers=(1, 14), prefill_T=8192),
 }
 
 

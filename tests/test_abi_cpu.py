@@ -140,3 +140,14 @@ def test_plan_rejects_bad_args(lib):
 def test_strerror_names_every_code(lib):
     for code in (bm.OK, bm.EINVAL, bm.EUNSUPPORTED, bm.EWORKSPACE, bm.EHIP, bm.EDEVICE):
         assert lib.bitmoe_strerror(code).startswith(b"BITMOE_")
+
+
+def test_residual_rescale_rejects_bad_args(lib):
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.bitmoe_residual_rescale(fake, fake, bm.BF16, 4, 4097, fake, None) == bm.EINVAL
+    assert lib.bitmoe_residual_rescale(fake, fake, bm.BF16, 4, 8, fake, None) == bm.EINVAL
+    assert lib.bitmoe_residual_rescale(fake, fake, 7, 4, 4096, fake, None) == bm.EUNSUPPORTED
+    assert lib.bitmoe_residual_rescale(None, fake, bm.BF16, 4, 4096, fake, None) == bm.EINVAL
+    assert lib.bitmoe_residual_rescale(None, None, bm.BF16, 0, 4096, None, None) == bm.OK
+    assert lib.bitmoe_residual_rescale(ctypes.c_void_p((1 << 20) + 4), fake, bm.F32, 4, 4096, fake, None) == bm.EINVAL
+    assert lib.bitmoe_residual_rescale(fake, fake, bm.F32, -1, 4096, fake, None) == bm.EINVAL

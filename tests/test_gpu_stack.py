@@ -1,0 +1,110 @@
+"""GPU parity of the resident 40-layer stack (sampled layers) and of its
+residual step, through the C ABI.
+
+The stack runs every layer on the device: route, experts + combine (bf16
+output), the Engram gather at its Engram layers, and the residual step
+x' = bf16((x + y) / rms(x + y)).  Sampled layers are checked against the
+oracle on the layer's own device input (so errors do not compound): expert
+ids up to the tie rule, outputs within 1e-2 per element, the residual step
+bit-exact, Engram rows bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import bit_moe_amd as bm
+import synthdata
+from oracle import compare, engram, formats, moe
+
+from gpu_util import device_layer, lut_device, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+SAMPLED = (0, 1, 14, 39)
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_tensor(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("y_f32", [False, True])
+@pytest.mark.parametrize("T,D", [(7, 4096), (3, 256), (0, 4096)])
+def test_residual_rescale_bit_exact(y_f32, T, D):
+    rng = np.random.default_rng(3 + T)
+    x = synthdata.bf16_bits_from_f32(rng.normal(size=(T, D)).astype(np.float32))
+    yf = (rng.normal(size=(T, D)) * 3).astype(np.float32)
+    if T > 1:
+        yf[1] = -formats.bf16_to_f64(x[1]).astype(np.float32)  # r = 0: the row rescales to zeros
+    if y_f32:
+        y_t, yv = torch.from_numpy(yf).cuda(), yf.astype(np.float64)
+    else:
+        yb = synthdata.bf16_bits_from_f32(yf)
+        y_t, yv = _bf16_tensor(yb), formats.bf16_to_f64(yb)
+    x_t = _bf16_tensor(x)
+    out = bm.residual_rescale(x_t, y_t)
+    ref = moe.residual_rescale(formats.bf16_to_f64(x), yv) if T else np.zeros((0, D), np.uint16)
+    assert np.array_equal(_bits(out), ref)
+    bm.residual_rescale(x_t, y_t, out=x_t)  # in place
+    assert np.array_equal(_bits(x_t), ref)
+
+
+@pytest.fixture(scope="module")
+def stack():
+    """The 40 layers (about 128 GB) and one Engram table per Engram layer,
+    filled on the device from the seeded streams."""
+    cfg = synthdata.CONFIGS["stack"]
+    lut = lut_device()
+    lds = [synthdata.LayerData(cfg, 1, l) for l in range(cfg.n_layers)]
+    layers = [device_layer(ld) for ld in lds]
+    tables = {}
+    for j, l in enumerate(cfg.engram_layers):
+        t = torch.empty(synthdata.ENGRAM_ROWS * 264, dtype=torch.uint8, device="cuda")
+        bm.fill(t, synthdata.tensor_key(1, synthdata.KIND_ENGRAM, j), bm.FILL_ENGRAM, lut)
+        tables[l] = (t.view(synthdata.ENGRAM_ROWS, 264), synthdata.tensor_key(1, synthdata.KIND_ENGRAM, j), j)
+    torch.cuda.synchronize()
+    yield cfg, lds, layers, tables
+    del layers, tables
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_stack_sampled_layers(stack, T):
+    cfg, lds, layers, tables = stack
+    x = torch.from_numpy(synthdata.activations_bf16(1, 40 + T, T, cfg.d_model).view(np.int16)).cuda()
+    x = x.view(torch.bfloat16)
+    toks = synthdata.token_ids(1, 50 + T, cfg.history + T)
+    rid = synthdata.engram_row_ids(1, toks, cfg.history)  # [T][2][8]: table j of Engram layer j
+    ws = bm.workspace(layers[0], T)
+    saved, rows = {}, {}
+    for l in range(cfg.n_layers):
+        ids, w = bm.route(layers[l], x, ws)
+        y = bm.expert_ffn(layers[l], x, ids, w, ws)
+        if l in tables:
+            t, key, j = tables[l]
+            rows[l] = (bm.engram_gather(t, torch.from_numpy(rid[:, j, :].copy()).cuda()), key, j)
+        xn = bm.residual_rescale(x, y)
+        if l in SAMPLED:
+            saved[l] = (x.clone(), ids.clone(), y.clone(), xn.clone())
+        x = xn
+    torch.cuda.synchronize()
+    print(f"[stack] T={T}: {cfg.n_layers} layers run")
+    for l in SAMPLED:
+        xin, ids, y, xn = saved[l]
+        xv = formats.bf16_to_f64(_bits(xin))
+        ids_h = ids.cpu().numpy()
+        r_ids, _, L = moe.route(xv, lds[l].router(), cfg.top_k)
+        _, _, bad = compare.compare_ids(ids_h, r_ids, L)
+        assert not bad, (l, bad)
+        ref = moe.moe_layer(oracle_layer(lds[l]), xv, ids=ids_h)
+        yv = formats.bf16_to_f64(_bits(y))
+        err = compare.max_rel_error(yv, ref.out)
+        print(f"[parity] stack layer {l} T={T} max rel err {err:.3e}")
+        assert err < TOL
+        assert np.array_equal(_bits(xn), moe.residual_rescale(xv, yv))
+    for l, (out, key, j) in rows.items():
+        ref = engram.gather(lambda r, k=key: synthdata.engram_rows(k, r), synthdata.ENGRAM_ROWS, rid[:, j, :])
+        assert compare.bf16_bits_equal(_bits(out), ref), l
