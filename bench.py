@@ -47,30 +47,19 @@ def log(msg: str) -> None:
 
 def algorithmic_bytes(T: int, U: float, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
     """Bytes the method must move per launch of each decode kernel that runs at
-    T tokens with U distinct experts: at T <= 2 the GEMV kernels hold routed and
-    shared rows, at T >= 3 the routed experts run on the MFMA kernels and the
-    GEMV kernels hold the shared expert only.  h travels as bf16 hi + lo."""
+    T tokens with U distinct experts: the router, the top-k, the gate/up and
+    down GEMV launches (each holding the routed experts' and the shared
+    expert's rows) and the combine.  h travels as bf16 hi + lo."""
     P = T * k
     x = T * D * 2
     h_pairs, h_tok = P * F * 2 * 2, T * F * 2 * 2
-    routed_gu = U * 2 * Q2_MAT + x + h_pairs
-    shared_gu = 2 * Q8_MAT + x + h_tok
-    routed_dn = U * Q2_MAT + h_pairs + P * D * 4
-    shared_dn = Q8_MAT + h_tok + T * D * 4
-    out = {
+    return {
         "router_gemv_kernel": E * D * 4 + x + T * E * 4,
         "topk_kernel": T * E * 4 + P * 8,
+        "ffn_gateup_kernel": U * 2 * Q2_MAT + 2 * Q8_MAT + x + h_pairs + h_tok,
+        "ffn_down_kernel": U * Q2_MAT + Q8_MAT + h_pairs + h_tok + (P + T) * D * 4,
         "combine_kernel": (P + T) * D * 4 + P * 8 + T * D * 2,
     }
-    if T <= 2:
-        out["ffn_gateup_kernel"] = routed_gu + shared_gu - x  # one activation read
-        out["ffn_down_kernel"] = routed_dn + shared_dn
-    else:
-        out["ffn_mfma_gateup_kernel"] = routed_gu
-        out["ffn_gateup_kernel"] = shared_gu
-        out["ffn_mfma_down_kernel"] = routed_dn
-        out["ffn_down_kernel"] = shared_dn
-    return out
 
 
 def source_hash(path: str) -> str:
@@ -78,9 +67,10 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(kernel_src: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+def stored_traffic(kernel_src: str, label: str):
+    """HBM bytes per launch of the kernel launched as `label`, from the
+    committed rocprofv3 counter summary, or None when the summary covers
+    another kernel or the kernel source changed since the counters were taken."""
     if not os.path.exists(PROFILE_SUMMARY):
         return None
     text = open(PROFILE_SUMMARY).read()
@@ -92,7 +82,7 @@ def stored_traffic(kernel_src: str):
                 if "=" in kv:
                     a, b = kv.split("=", 1)
                     vals[a] = b
-    if vals.get("source_sha") != want or "traffic_bytes" not in vals:
+    if vals.get("source_sha") != want or "traffic_bytes" not in vals or vals.get("label") != label:
         return None
     return float(vals["traffic_bytes"])
 
@@ -232,7 +222,8 @@ def bench_verify(bm, torch, np, synthdata, args, lut, dev) -> dict:
     step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
     alg = algorithmic_bytes(T, U_mean)
     alg["engram_gather_kernel"] = T * 8 * (264 + 512) + T * 8 * 8
-    step_bytes = sum(alg.values()) - alg["engram_gather_kernel"] + 2 * alg["engram_gather_kernel"]
+    # bytes of the kernels that ran (the Engram kernel runs twice per step)
+    step_bytes = sum(alg[n] * prof[n][1] for n in prof if n in alg) / K
     return {"workload": "verify batch T=5 (+3 history tokens) through one decode layer, plus 2 x 8 Engram rows "
                         "per token gathered from two 2^22-row tables",
             "tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 5),
@@ -443,10 +434,10 @@ def main() -> int:
     dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
     achieved = alg[dom] / dom_avg_s / 1e9
     src = os.path.join(ROOT, "bit_moe_amd", "csrc", "gemv.hip")
-    traffic = stored_traffic(src) if dom in ("ffn_gateup_kernel", "ffn_mfma_gateup_kernel") else None
+    traffic = stored_traffic(src, dom)
     step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
     value = T / (step_ms * 1e-3)
-    step_bytes = sum(alg.values())
+    step_bytes = sum(alg[n] * prof[n][1] for n in prof if n in alg) / K  # bytes of the kernels that ran
     out = {
         "metric": METRIC,
         "value": round(value, 1),

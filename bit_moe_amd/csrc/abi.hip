@@ -106,6 +106,39 @@ void carve_decode(Carve &c, const bitmoe_layer *L, int T, DecodeWs *w) {
   w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
 }
 
+// Decode-path kernel arguments over the workspace carve (after the common region).
+bm::FfnArgs decode_args(Carve &c, const bitmoe_layer *L, const void *x, int T, const int32_t *ids, const float *wts,
+                        void *y, int y_dtype, int64_t *status) {
+  DecodeWs w;
+  carve_decode(c, L, T, &w);
+  const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
+  bm::FfnArgs a{};
+  a.D = L->d_model;
+  a.F = L->d_ff;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.T = T;
+  a.wg = static_cast<const uint8_t *>(L->w_gate);
+  a.wu = static_cast<const uint8_t *>(L->w_up);
+  a.wd = static_cast<const uint8_t *>(L->w_down);
+  a.sg = shared ? static_cast<const uint8_t *>(L->ws_gate) : nullptr;
+  a.su = shared ? static_cast<const uint8_t *>(L->ws_up) : nullptr;
+  a.sd = shared ? static_cast<const uint8_t *>(L->ws_down) : nullptr;
+  a.x = x;
+  a.ids = ids;
+  a.wts = wts;
+  a.h = w.h;
+  a.hs = w.hs;
+  a.h_lo = w.h_lo;
+  a.hs_lo = w.hs_lo;
+  a.y = w.y;
+  a.ys = w.ys;
+  a.out = y;
+  a.out_bf16 = y_dtype == BITMOE_BF16;
+  a.status = status;
+  return a;
+}
+
 void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   const int E = L->n_experts;
   const size_t P = size_t(T) * L->top_k;
@@ -234,32 +267,7 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   carve_common(c, L, T, &status, nullptr);
   const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
   if (m == BITMOE_MODE_DECODE) {
-    DecodeWs w;
-    carve_decode(c, L, T, &w);
-    bm::FfnArgs a{};
-    a.D = L->d_model;
-    a.F = L->d_ff;
-    a.E = L->n_experts;
-    a.k = L->top_k;
-    a.T = T;
-    a.wg = static_cast<const uint8_t *>(L->w_gate);
-    a.wu = static_cast<const uint8_t *>(L->w_up);
-    a.wd = static_cast<const uint8_t *>(L->w_down);
-    a.sg = shared ? static_cast<const uint8_t *>(L->ws_gate) : nullptr;
-    a.su = shared ? static_cast<const uint8_t *>(L->ws_up) : nullptr;
-    a.sd = shared ? static_cast<const uint8_t *>(L->ws_down) : nullptr;
-    a.x = x;
-    a.ids = topk_ids;
-    a.wts = topk_w;
-    a.h = w.h;
-    a.hs = w.hs;
-    a.h_lo = w.h_lo;
-    a.hs_lo = w.hs_lo;
-    a.y = w.y;
-    a.ys = w.ys;
-    a.out = y;
-    a.out_bf16 = y_dtype == BITMOE_BF16;
-    a.status = status;
+    const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
     hipError_t e = bm::launch_decode_ffn(a, x_dtype == BITMOE_F32, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
     return BITMOE_OK;

@@ -114,6 +114,24 @@ BM_DEVICE float wave_sum(float v) {
 
 BM_DEVICE float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// ---- direct-to-LDS copies ----------------------------------------------------
+// 16 bytes per lane from global p into LDS at byte offset lds + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the wave's LDS base and is set here).
+// Issued from asm on purpose: for the builtin the compiler waits for every
+// load in flight before any later LDS read, which would serialise a
+// prefetch with the reads of the buffer before it.  Completion is therefore
+// the caller's business: an explicit s_waitcnt vmcnt (loads of one wave
+// complete in issue order), plus a barrier when other waves read the data.
+BM_DEVICE void lds_dma16(const void *p, uint32_t lds) {
+  // lds is wave-uniform; readfirstlane puts it in an SGPR when the compiler cannot tell
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(base) : "memory");
+}
+// LDS byte offset of a generic pointer into shared memory
+BM_DEVICE uint32_t lds_offset(const void *p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
 // ---- sticky device status record (int64 code flags, int64 detail) --------
 // detail stores INT64_MAX - index so that atomicMax keeps the smallest index
 // while a zero-filled record means "nothing recorded".

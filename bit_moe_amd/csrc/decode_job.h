@@ -43,6 +43,29 @@ BM_DEVICE bool pair_job(const FfnArgs &a, int p, Job &job) {
   return true;
 }
 
+// pair_job for a block of one wave: the call's pair ids are read by the lanes
+// (T * k <= 64) and matched with one ballot.
+BM_DEVICE bool pair_job_wave(const FfnArgs &a, int p, Job &job) {
+  const int P = a.T * a.k;
+  if (P > 64) return pair_job(a, p, job);
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) return false;
+  const int lane = threadIdx.x & 63;
+  const int id = lane < P ? a.ids[lane] : -1;
+  uint64_t m = __ballot(id == e);
+  if (m & ((uint64_t(1) << p) - 1)) return false;  // an earlier pair chose e
+  job.e = e;
+  job.n = 0;
+  job.pairs = 0;
+  while (m != 0 && job.n < 8) {
+    const int q = __builtin_ctzll(m);
+    m &= m - 1;
+    job.pairs |= uint64_t(q) << (8 * job.n);
+    ++job.n;
+  }
+  return true;
+}
+
 BM_DEVICE void shared_job(const FfnArgs &a, Job &job) {
   job.e = -1;
   job.n = a.T;

@@ -17,6 +17,9 @@
 //  ffn_down_kernel    same shape over the down matrices, y = Wd h in float32
 //                     per (token, slot) pair and per token for the shared one;
 //                     the hi and lo parts of h are two bf16 operand streams.
+//  ffn_stream_kernel  (T >= 2) either half over one-wave blocks that stream
+//                     their chunk of rows through an LDS ring with coalesced
+//                     direct-to-LDS loads (details at the kernel).
 //  combine_kernel     out[t] = sum_j w[t,j] y[t,j] + y_shared[t], j in order,
 //                     rounded once.
 //
@@ -36,7 +39,6 @@
 #include <type_traits>
 
 #include "decode_job.h"
-#include "mfma_q2.h"
 
 namespace bm {
 
@@ -172,9 +174,7 @@ BM_DEVICE int stage_bytes(uint8_t *dst, const uint8_t *src, int nbytes) {
   const int lane = threadIdx.x & 63, wave0 = threadIdx.x & ~63;
   for (int c0 = wave0; c0 < n16; c0 += blockDim.x) {
     if (c0 + lane < n16)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(base + 16 * (c0 + lane)),
-                                       (__attribute__((address_space(3))) void *)(dst + 16 * c0),
-                                       16, 0, 0);
+      lds_dma16(base + 16 * (c0 + lane), lds_offset(dst + 16 * c0));
   }
   return pad;
 }
@@ -373,8 +373,10 @@ BM_DEVICE void down_block(const FfnArgs &a, const Job &job, int t0, int nt, int 
 }
 
 // Grid: the shared expert's row chunks first, then u_max routed job slots x
-// row chunks; every job's pairs in passes of NT.
-template <int NT>
+// row chunks.  The shared job's tokens go in passes of NT_S; a routed job with
+// one pair (the common case of a verify batch) takes the one-token code, else
+// its pairs go in passes of NT_R.
+template <int NT_S, int NT_R>
 __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_down[];
   Job job;
@@ -390,12 +392,12 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
     r0 = (b % a.chunks_dn) * a.rows_dn;
     nrows = min(a.rows_dn, a.D - r0);
   }
-  for (int t0 = 0; t0 < job.n; t0 += NT) {
-    const int nt = min(NT, job.n - t0);
-    if (shared)
-      down_block<true, NT>(a, job, t0, nt, r0, nrows, smem_down);
-    else
-      down_block<false, NT>(a, job, t0, nt, r0, nrows, smem_down);
+  if (shared) {
+    for (int t0 = 0; t0 < job.n; t0 += NT_S) down_block<true, NT_S>(a, job, t0, min(NT_S, job.n - t0), r0, nrows, smem_down);
+  } else if (NT_R == 1 || job.n == 1) {
+    for (int t0 = 0; t0 < job.n; ++t0) down_block<false, 1>(a, job, t0, 1, r0, nrows, smem_down);
+  } else {
+    for (int t0 = 0; t0 < job.n; t0 += NT_R) down_block<false, NT_R>(a, job, t0, min(NT_R, job.n - t0), r0, nrows, smem_down);
   }
 }
 
@@ -722,7 +724,9 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
 
 // Grid: the shared expert's row chunks first (its Q8_0 rows are the heaviest,
 // so they start first), then u_max routed job slots x chunks_gu row chunks.
-template <int NT, bool XF32>
+// Token passes as in the down kernel: NT_S for the shared job, one-token code
+// for a routed job of one pair, else passes of NT_R.
+template <int NT_S, int NT_R, bool XF32>
 __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
   Job job;
   int r_begin, r_end;
@@ -737,12 +741,14 @@ __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
     r_begin = (b % a.chunks_gu) * a.rows_gu;
     r_end = min(a.F, r_begin + a.rows_gu);
   }
-  for (int t0 = 0; t0 < job.n; t0 += NT) {
-    const int nt = min(NT, job.n - t0);
-    if (shared)
-      gateup_rows<NT, XF32, true>(a, job, t0, nt, r_begin, r_end);
-    else
-      gateup_rows<NT, XF32, false>(a, job, t0, nt, r_begin, r_end);
+  if (shared) {
+    for (int t0 = 0; t0 < job.n; t0 += NT_S)
+      gateup_rows<NT_S, XF32, true>(a, job, t0, min(NT_S, job.n - t0), r_begin, r_end);
+  } else if (NT_R == 1 || job.n == 1) {
+    for (int t0 = 0; t0 < job.n; ++t0) gateup_rows<1, XF32, false>(a, job, t0, 1, r_begin, r_end);
+  } else {
+    for (int t0 = 0; t0 < job.n; t0 += NT_R)
+      gateup_rows<NT_R, XF32, false>(a, job, t0, min(NT_R, job.n - t0), r_begin, r_end);
   }
 }
 
@@ -767,7 +773,7 @@ static size_t down_smem(bool q8, int K, int rows, int nt) {
 // Gate/up GEMV launch over the shared expert's row chunks and u_max routed
 // job slots: routed blocks hold 4 row iterations per wave, shared (Q8_0, 3.2x
 // the bytes per row) blocks 2.
-template <int NT, bool XF32>
+template <int NT_S, int NT_R, bool XF32>
 static hipError_t launch_gateup_gemv(FfnArgs a, hipStream_t stream) {
   const int rpi = 64 / (a.D / 64);
   a.rows_gu = min(a.F, 16 * rpi);
@@ -776,249 +782,275 @@ static hipError_t launch_gateup_gemv(FfnArgs a, hipStream_t stream) {
   a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
   const unsigned grid = unsigned(a.chunks_sg + a.u_max * a.chunks_gu);
   if (grid == 0) return hipSuccess;
-  BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT, XF32>), dim3(grid), dim3(256), 0, stream, a);
+  BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_kernel<NT_S, NT_R, XF32>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 // Down GEMV launch over the shared expert's row chunks and u_max routed job
 // slots; raises the kernel's LDS limit when needed.
-template <int NT>
+template <int NT_S, int NT_R>
 static hipError_t launch_down_gemv(FfnArgs a, hipStream_t stream) {
-  a.rows_dn = down_rows(false, a.F, a.D, NT);
+  a.rows_dn = down_rows(false, a.F, a.D, NT_R);
   a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
-  a.rows_sd = down_rows(true, a.F, a.D, NT);
+  a.rows_sd = down_rows(true, a.F, a.D, NT_S);
   a.chunks_sd = a.sd ? (a.D + a.rows_sd - 1) / a.rows_sd : 0;
-  const size_t smem = std::max(a.u_max ? down_smem(false, a.F, a.rows_dn, NT) : 0,
-                               a.sd ? down_smem(true, a.F, a.rows_sd, NT) : 0);
+  const size_t smem = std::max(a.u_max ? down_smem(false, a.F, a.rows_dn, NT_R) : 0,
+                               a.sd ? down_smem(true, a.F, a.rows_sd, NT_S) : 0);
   const unsigned grid = unsigned(a.chunks_sd + a.u_max * a.chunks_dn);
   if (grid == 0) return hipSuccess;
   if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_down_kernel<NT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&ffn_down_kernel<NT_S, NT_R>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
   }
-  BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT>), dim3(grid), dim3(256), smem, stream, a);
+  BM_LAUNCH("ffn_down_kernel", (ffn_down_kernel<NT_S, NT_R>), dim3(grid), dim3(256), smem, stream, a);
   return hipGetLastError();
 }
 
-// ---- routed experts on MFMA (decode) ------------------------------------------
-// Routed jobs: (union slot, 16 output rows).  The 4 waves split the K range
-// (super-blocks) of the block's 16 weight rows and reduce their 16x16 partial
-// tiles in LDS.  The job's tokens (up to np per pass) are staged in LDS with
-// their sub-block sums, so every token of the job uses the same dequantised
-// operands (the union is read once).  Shared-expert blocks (Q8_0) run the GEMV
-// rows of the same kernel launch.
-//
-// GATEUP: A = x (bf16, or float32 split into hi + lo), two weight matrices,
-// SwiGLU epilogue -> h hi/lo.  Down: A = h hi + lo, one matrix -> y float32.
+// ---- streamed GEMV: each wave stages its rows through an LDS ring ------------
+// A block is one wave that owns one job and a chunk of at most 64 consecutive
+// output rows.  The weight bytes of the chunk are consumed in stages of 64
+// units (RPI rows of one matrix: 1344 bytes of Q2 or 4352 bytes of Q8_0),
+// copied into a wave-private LDS ring with 16-byte direct-to-LDS loads, so
+// every load instruction reads 1 KB of contiguous HBM; up to NBUF stages are
+// in flight.  Lane l computes unit l of the stage against its tokens'
+// activation operands (registers), the LPR lanes of each row are summed, and
+// the row's value is parked in lane (row - chunk start) until one coalesced
+// store per token at the end.  The global loads of the wave complete in issue
+// order, so waiting for all but the stages issued after stage j (NI loads per
+// stage) makes stage j visible in LDS; no store is issued inside the loop.
 
-struct MfmaDecodeCfg {
-  int np;     // tokens per pass (LDS rows)
-  int parts;  // 1: A is bf16; 2: A arrives as hi + lo parts
+constexpr int RING_BYTES = 13 * 1024;  // LDS ring per wave
+constexpr int STREAM_ROWS_GU = 8, STREAM_ROWS_SG = 8;   // rows per chunk, gate/up (routed, shared)
+constexpr int STREAM_ROWS_DN = 16, STREAM_ROWS_SD = 16;  // down
+constexpr int LAYER_ROWS_SG = 2, LAYER_ROWS_SD = 4;      // shared rows per wave beside the router / top-k
+
+template <int K, bool IS_Q8>
+struct StreamGeo {
+  static constexpr int LPR = K / 64, RPI = 64 / LPR;
+  static constexpr int ROWB = IS_Q8 ? K / 32 * 34 : K / 256 * 84;  // bytes per weight row
+  static constexpr int STB = RPI * ROWB;                            // stage bytes (64 units)
+  static constexpr int NI = (STB + 1023) / 1024;                    // loads per lane per stage
+  static constexpr int NBUF = RING_BYTES / STB;                     // ring depth
+  static_assert(STB % 16 == 0 && NBUF >= 2 && NI * (NBUF - 1) <= 63, "stream geometry");
 };
 
-template <bool GATEUP, bool XF32>
-BM_DEVICE void routed_mfma_rows(const FfnArgs &a, const Job &job, int chunk, int np_max, char *smem) {
-  constexpr int PARTS = (GATEUP && !XF32) ? 1 : 2;
-  const int K = GATEUP ? a.D : a.F, N = GATEUP ? a.F : a.D;
-  const int nsb = K / 256;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, nl = lane & 15, p = g & 1;
-  const int r0 = chunk * 16, n = r0 + nl;
-  // LDS carve: A parts, sub-block sums, sc tables, reduction tiles
-  uint16_t *As = reinterpret_cast<uint16_t *>(smem);
-  uint16_t *Al = As + size_t(np_max) * K;
-  uint16_t *Xs = As + size_t(PARTS) * np_max * K;             // [np][nsb][32]
-  uint2 *tab = reinterpret_cast<uint2 *>(Xs + size_t(np_max) * nsb * 32);
-  float *red = reinterpret_cast<float *>(tab + 16);            // [4][2][256]
-  if (tid < 16) tab[tid] = sc_table_entry(tid);
-  const size_t mat_bytes = size_t(a.F) * a.D / 256 * 84;
-  const uint8_t *w0 = (GATEUP ? a.wg : a.wd) + size_t(job.e) * mat_bytes + size_t(n) * (K / 256) * 84;
-  const uint8_t *w1 = GATEUP ? a.wu + size_t(job.e) * mat_bytes + size_t(n) * (K / 256) * 84 : nullptr;
-  const int sb0 = wave * nsb / 4, sb1 = (wave + 1) * nsb / 4;
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  // two super-blocks of weights in flight per wave (current + next), the first
-  // two issued before the activations are staged
-  Q2Raw c0, c1, n0, n1;
-  auto load_sb = [&](int sb, Q2Raw &r0, Q2Raw &r1) {
-    r0 = q2_load(w0 + size_t(sb) * 84, g);
-    if constexpr (GATEUP) r1 = q2_load(w1 + size_t(sb) * 84, g);
-  };
-  if (sb0 < sb1) load_sb(sb0, c0, c1);
-  if (sb0 + 1 < sb1) load_sb(sb0 + 1, n0, n1);
-
-  for (int t0 = 0; t0 < job.n; t0 += np_max) {
-    const int np = min(np_max, job.n - t0);
-    __syncthreads();  // LDS of the previous pass is consumed
-    // stage the A rows (8 bf16 per thread-iteration)
-    const int k8 = K / 8;
-    for (int idx = tid; idx < np * k8; idx += 256) {
-      const int row = idx / k8, c = (idx % k8) * 8;
-      uint4 hi, lo = make_uint4(0u, 0u, 0u, 0u);
-      if constexpr (GATEUP) {
-        const int tok = jtok(a, job, t0 + row);
-        if constexpr (XF32) {
-          const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) + size_t(tok) * K + c);
-          const float4 f0 = src[0], f1 = src[1];
-          const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-          uint32_t hb[8], lb[8];
+// copy one stage (STB bytes at src, 16-byte aligned) into LDS at slot
+template <int STB, int NI>
+BM_DEVICE void stream_issue(uint8_t *slot, const uint8_t *src) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = lds_offset(slot);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            hb[i] = f32_to_bf16(f[i]);
-            lb[i] = f32_to_bf16(f[i] - bf16_to_f32(uint16_t(hb[i])));
-          }
-          hi = make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
-          lo = make_uint4(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16);
-        } else {
-          hi = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) + size_t(tok) * K + c);
-        }
+  for (int i = 0; i < NI; ++i)
+    if (i * 1024 + lane * 16 < STB) lds_dma16(src + i * 1024 + lane * 16, base + i * 1024);
+}
+
+template <int N>
+BM_DEVICE void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `ahead` stages of NI loads each are outstanding
+template <int NI, int MAXA>
+BM_DEVICE void stream_wait(int ahead) {
+  if constexpr (MAXA > 0) {
+    if (ahead >= MAXA) {
+      vm_wait<NI * MAXA>();
+      return;
+    }
+    stream_wait<NI, MAXA - 1>(ahead);
+  } else {
+    vm_wait<0>();
+  }
+}
+
+// Rows [r_begin, r_end) (a multiple of RPI rows, at most 64) of one job for its
+// tokens / pairs t0 .. t0 + nt - 1.  GATEUP: gate and up matrices, operands
+// from x, h = silu(g) u stored as hi + lo; down: operands from h hi + lo, y.
+template <int K, int NT, bool GATEUP, bool XF32, bool IS_Q8>
+BM_DEVICE void stream_rows(const FfnArgs &a, const Job &job, int t0, int nt, int r_begin, int r_end, uint8_t *ring) {
+  using G = StreamGeo<K, IS_Q8>;
+  constexpr int PARTS = GATEUP ? (XF32 ? 2 : 1) : 2;
+  constexpr int NV = NT * PARTS;
+  constexpr int NM = GATEUP ? 2 : 1;
+  const int lane = threadIdx.x & 63;
+  const int jj = lane % G::LPR;
+  // activation operands of the lane's unit (its columns do not depend on the row)
+  const int c0 = IS_Q8 ? jj * 64 : q2_c0(jj >> 2, jj & 3, K);
+  typename std::conditional<IS_Q8, XQ8, XQ2>::type X[NV];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const int ti = t0 + min(i, nt - 1);
+    if constexpr (GATEUP) {
+      const size_t row = size_t(jtok(a, job, ti)) * K;
+      if constexpr (IS_Q8) {
+        if constexpr (XF32)
+          load_xq8_f32(static_cast<const float *>(a.x) + row, c0, X[2 * i], X[2 * i + 1]);
+        else
+          load_xq8_bf16(static_cast<const uint16_t *>(a.x) + row, c0, X[i]);
       } else {
-        const size_t pr = size_t(jpair(job, t0 + row));
-        hi = *reinterpret_cast<const uint4 *>(a.h + pr * K + c);
-        lo = *reinterpret_cast<const uint4 *>(a.h_lo + pr * K + c);
+        if constexpr (XF32)
+          load_xq2_f32(static_cast<const float *>(a.x) + row, c0, X[2 * i], X[2 * i + 1]);
+        else
+          load_xq2_bf16(static_cast<const uint16_t *>(a.x) + row, c0, X[i]);
       }
-      *reinterpret_cast<uint4 *>(As + size_t(row) * K + c) = hi;
-      if constexpr (PARTS == 2) *reinterpret_cast<uint4 *>(Al + size_t(row) * K + c) = lo;
-    }
-    __syncthreads();
-    // sub-block sums of the staged rows (hi + lo), split into bf16 hi + lo
-    const int k16 = K / 16;
-    for (int idx = tid; idx < np * k16; idx += 256) {
-      const int row = idx / k16, sbk = idx % k16;
-      const uint16_t *src = As + size_t(row) * K + sbk * 16;
-      float sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += bf16_to_f32(src[i]);
-      if constexpr (PARTS == 2) {
-        const uint16_t *sl = Al + size_t(row) * K + sbk * 16;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum += bf16_to_f32(sl[i]);
-      }
-      const uint16_t shi = f32_to_bf16(sum);
-      uint16_t *dst = Xs + (size_t(row) * nsb + (sbk >> 4)) * 32;
-      dst[q2_sum_slot(sbk & 15, 0)] = shi;
-      dst[q2_sum_slot(sbk & 15, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
-    }
-    __syncthreads();
-    // this wave's super-blocks
-    const bool arow = nl < np;  // lane supplies A row nl
-    f32x4_t acc0 = zero, acc1 = zero;
-    if (t0 > 0 && sb0 < sb1) {  // another pass over the same rows: reload the pipeline
-      load_sb(sb0, c0, c1);
-      if (sb0 + 1 < sb1) load_sb(sb0 + 1, n0, n1);
-    }
-    for (int sb = sb0; sb < sb1; ++sb) {
-      const Q2Raw r0w = c0;
-      const Q2Raw r1w = c1;
-      c0 = n0;
-      c1 = n1;
-      if (sb + 2 < sb1) load_sb(sb + 2, n0, n1);
-      f32x4_t cm0 = zero, cm1 = zero;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int kk = sb * 256 + q2_kofs(t, g);
-        uint32_t A[4] = {0u, 0u, 0u, 0u}, B0[4], B1[4];
-        if (arow) ld16(As + size_t(nl) * K + kk, A);
-        q2_main_operand(r0w, p, t, tab, B0);
-        cm0 = mfma16(A, B0, cm0);
-        if constexpr (GATEUP) {
-          q2_main_operand(r1w, p, t, tab, B1);
-          cm1 = mfma16(A, B1, cm1);
-        }
-        if constexpr (PARTS == 2) {
-          if (arow) ld16(Al + size_t(nl) * K + kk, A);
-          cm0 = mfma16(A, B0, cm0);
-          if constexpr (GATEUP) cm1 = mfma16(A, B1, cm1);
-        }
-      }
-      uint32_t As_[4] = {0u, 0u, 0u, 0u}, Bn0[4], Bn1[4];
-      if (arow) ld16(Xs + (size_t(nl) * nsb + sb) * 32 + 8 * g, As_);
-      q2_min_operand(r0w, p, Bn0);
-      const f32x4_t cn0 = mfma16(As_, Bn0, zero);
-      const float d0 = q2_d(r0w), dm0 = q2_dmin(r0w);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc0[r] = __builtin_fmaf(d0, cm0[r], __builtin_fmaf(-dm0, cn0[r], acc0[r]));
-      if constexpr (GATEUP) {
-        q2_min_operand(r1w, p, Bn1);
-        const f32x4_t cn1 = mfma16(As_, Bn1, zero);
-        const float d1 = q2_d(r1w), dm1 = q2_dmin(r1w);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc1[r] = __builtin_fmaf(d1, cm1[r], __builtin_fmaf(-dm1, cn1[r], acc1[r]));
+    } else {
+      const size_t row = size_t(IS_Q8 ? jtok(a, job, ti) : jpair(job, ti)) * K;
+      const uint16_t *hi = IS_Q8 ? a.hs : a.h, *lo = IS_Q8 ? a.hs_lo : a.h_lo;
+      if constexpr (IS_Q8) {
+        load_xq8_bf16(hi + row, c0, X[2 * i]);
+        load_xq8_bf16(lo + row, c0, X[2 * i + 1]);
+      } else {
+        load_xq2_bf16(hi + row, c0, X[2 * i]);
+        load_xq2_bf16(lo + row, c0, X[2 * i + 1]);
       }
     }
-    // reduce the 4 waves' tiles: element (m = 4g + r, column nl)
+  }
+  const uint8_t *m0, *m1 = nullptr;
+  if constexpr (IS_Q8) {
+    m0 = GATEUP ? a.sg : a.sd;
+    if constexpr (GATEUP) m1 = a.su;
+  } else {
+    const size_t mat = size_t(a.F) * a.D / 256 * 84;
+    m0 = (GATEUP ? a.wg : a.wd) + size_t(job.e) * mat;
+    if constexpr (GATEUP) m1 = a.wu + size_t(job.e) * mat;
+  }
+  // stage j: row group j / NM (rows r_begin + (j / NM) RPI ..), matrix j % NM
+  const int n_st = (r_end - r_begin) / G::RPI * NM;
+  auto src = [&](int j) {
+    return ((NM == 2 && (j & 1)) ? m1 : m0) + size_t(r_begin + (j / NM) * G::RPI) * G::ROWB;
+  };
+  for (int j = 0; j < G::NBUF && j < n_st; ++j) stream_issue<G::STB, G::NI>(ring + j * G::STB, src(j));
+  float res[NT], gsum[NT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      red[(wave * 2 + 0) * 256 + (4 * g + r) * 16 + nl] = acc0[r];
-      if constexpr (GATEUP) red[(wave * 2 + 1) * 256 + (4 * g + r) * 16 + nl] = acc1[r];
-    }
-    __syncthreads();
-    {
-      const int m = tid >> 4, c = tid & 15;
-      if (m < np) {
-        float v0 = 0.f, v1 = 0.f;
+  for (int i = 0; i < NT; ++i) res[i] = gsum[i] = 0.f;
+  // SPI stages per iteration (two for Q2: a gate row with its up row, or two
+  // row groups of down), so that their arithmetic and row sums interleave
+  constexpr int SPI = IS_Q8 ? 1 : 2;
+  for (int j = 0; j < n_st; j += SPI) {
+    const int nj = min(SPI, n_st - j);
+    // stages j .. j + nj - 1 have landed; later ones may still be in flight
+    stream_wait<G::NI, G::NBUF - 1>(min(G::NBUF - nj, n_st - j - nj));
+    float acc[SPI][NV];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v0 += red[(w * 2 + 0) * 256 + m * 16 + c];
-          if constexpr (GATEUP) v1 += red[(w * 2 + 1) * 256 + m * 16 + c];
-        }
-        if constexpr (GATEUP) {
-          const float hf = silu(v0) * v1;
-          const uint16_t hb = f32_to_bf16(hf);
-          const size_t o = size_t(jpair(job, t0 + m)) * a.F + r0 + c;
-          a.h[o] = hb;
-          a.h_lo[o] = f32_to_bf16(hf - bf16_to_f32(hb));
+    for (int q = 0; q < SPI; ++q) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[q][v] = 0.f;
+      if (q < nj) {
+        const uint8_t *slot = ring + ((j + q) % G::NBUF) * G::STB;
+        if constexpr (IS_Q8) {
+          const Q8Unit u = q8_unit_load(slot + lane * 68);
+          q8_unit_dot<NV>(u, X, acc[q]);
         } else {
-          a.y[size_t(jpair(job, t0 + m)) * a.D + r0 + c] = v0;
+          const Q2Unit u = q2_unit_load(slot + (lane >> 2) * 84, (lane >> 1) & 1, lane & 1);
+          q2_unit_dot<NV>(u, lane & 1, X, acc[q]);
         }
       }
     }
-    (void)N;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slots' LDS reads are done before their refill
+#pragma unroll
+    for (int q = 0; q < SPI; ++q)
+      if (q < nj && j + q + G::NBUF < n_st)
+        stream_issue<G::STB, G::NI>(ring + ((j + q) % G::NBUF) * G::STB, src(j + q + G::NBUF));
+    float vs[SPI][NT];
+#pragma unroll
+    for (int q = 0; q < SPI; ++q)
+#pragma unroll
+      for (int i = 0; i < NT; ++i)  // every lane of a row's group gets the row's sum
+        vs[q][i] = lane_group_sum(PARTS == 2 ? acc[q][2 * i] + acc[q][2 * i + 1] : acc[q][i], G::LPR);
+#pragma unroll
+    for (int q = 0; q < SPI; ++q) {
+      if (q >= nj) break;
+      const int js = j + q, rg = js / NM;
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        if (GATEUP && (js % NM) == 0) {
+          gsum[i] = vs[q][i];
+          continue;
+        }
+        const float rv = GATEUP ? silu(gsum[i]) * vs[q][i] : vs[q][i];
+        // row rg * RPI + r lives in lanes r * LPR ..; park it in lane (row - r_begin)
+#pragma unroll
+        for (int r = 0; r < G::RPI; ++r) {
+          const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rv), r * G::LPR));
+          if (lane == rg * G::RPI + r) res[i] = s;
+        }
+      }
+    }
+  }
+  const int nrows = r_end - r_begin;
+  if (lane < nrows) {
+    const int r = r_begin + lane;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      if (i >= nt) break;
+      if constexpr (GATEUP) {
+        const size_t o = size_t(IS_Q8 ? jtok(a, job, t0 + i) : jpair(job, t0 + i)) * a.F + r;
+        // h travels as bf16 hi + lo parts (h - hi is exact in float32)
+        const uint16_t hv = f32_to_bf16(res[i]);
+        (IS_Q8 ? a.hs : a.h)[o] = hv;
+        (IS_Q8 ? a.hs_lo : a.h_lo)[o] = f32_to_bf16(res[i] - bf16_to_f32(hv));
+      } else {
+        if constexpr (IS_Q8)
+          a.ys[size_t(jtok(a, job, t0 + i)) * a.D + r] = res[i];
+        else
+          a.y[size_t(jpair(job, t0 + i)) * a.D + r] = res[i];
+      }
+    }
   }
 }
 
-template <bool GATEUP, bool XF32>
-__global__ void __launch_bounds__(256) ffn_mfma_decode_kernel(FfnArgs a, MfmaDecodeCfg cfg) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+// Grid: the shared expert's row chunks first, then u_max routed job slots x
+// row chunks (chunks_sg / rows_sg and chunks_gu / rows_gu for gate/up,
+// chunks_sd / rows_sd and chunks_dn / rows_dn for down).  Token passes: NT_S
+// for the shared job, the one-token code for a routed job of one pair, else
+// passes of NT_R.
+template <int K, int NT_S, int NT_R, bool GATEUP, bool XF32>
+__global__ void __launch_bounds__(64) ffn_stream_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RING_BYTES];
+  const int chunks_s = GATEUP ? a.chunks_sg : a.chunks_sd, rows_s = GATEUP ? a.rows_sg : a.rows_sd;
+  const int chunks_r = GATEUP ? a.chunks_gu : a.chunks_dn, rows_r = GATEUP ? a.rows_gu : a.rows_dn;
+  const int N = GATEUP ? a.F : a.D;
   Job job;
-  const int chunks = (GATEUP ? a.F : a.D) / 16;
-  if (!pair_job(a, blockIdx.x / chunks, job)) return;
-  routed_mfma_rows<GATEUP, XF32>(a, job, blockIdx.x % chunks, cfg.np, smem);
+  int r_begin, r_end;
+  const bool shared = int(blockIdx.x) < chunks_s;
+  if (shared) {
+    shared_job(a, job);
+    r_begin = blockIdx.x * rows_s;
+    r_end = min(N, r_begin + rows_s);
+  } else {
+    const int b = blockIdx.x - chunks_s;
+    if (!pair_job_wave(a, b / chunks_r, job)) return;
+    r_begin = (b % chunks_r) * rows_r;
+    r_end = min(N, r_begin + rows_r);
+  }
+  if (shared) {
+    for (int t0 = 0; t0 < job.n; t0 += NT_S)
+      stream_rows<K, NT_S, GATEUP, XF32, true>(a, job, t0, min(NT_S, job.n - t0), r_begin, r_end, ring);
+  } else if (NT_R == 1 || job.n == 1) {
+    for (int t0 = 0; t0 < job.n; ++t0) stream_rows<K, 1, GATEUP, XF32, false>(a, job, t0, 1, r_begin, r_end, ring);
+  } else {
+    for (int t0 = 0; t0 < job.n; t0 += NT_R)
+      stream_rows<K, NT_R, GATEUP, XF32, false>(a, job, t0, min(NT_R, job.n - t0), r_begin, r_end, ring);
+  }
 }
 
-static size_t mfma_decode_smem(int K, int np, int parts) {
-  const int nsb = K / 256;
-  return size_t(parts) * np * K * 2 + size_t(np) * nsb * 32 * 2 + 16 * 8 + 4 * 2 * 256 * 4;
-}
-
-// Routed experts on MFMA; the shared expert (Q8_0) on the GEMV kernels with no
-// routed jobs (u_max = 0): separate launches, so each gets its own registers.
-template <int NT, bool XF32>
-static hipError_t launch_mfma_decode(const FfnArgs &a, hipStream_t stream) {
-  const size_t cap = 56 * 1024;
-  FfnArgs sh = a;
-  sh.u_max = 0;  // shared row chunks only
-  hipError_t err;
-  {  // gate/up
-    const int parts = XF32 ? 2 : 1;
-    const size_t per_row = size_t(parts) * a.D * 2 + size_t(a.D / 256) * 64;
-    const size_t fit = (cap - 8320) / per_row;
-    MfmaDecodeCfg c{int(std::max<size_t>(1, std::min<size_t>(size_t(std::min(a.T, 16)), fit))), parts};
-    BM_LAUNCH("ffn_mfma_gateup_kernel", (ffn_mfma_decode_kernel<true, XF32>), dim3(a.u_max * (a.F / 16)), dim3(256),
-              mfma_decode_smem(a.D, c.np, parts), stream, a, c);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sg && (err = launch_gateup_gemv<NT, XF32>(sh, stream)) != hipSuccess) return err;
+// Streamed launch of one half of the FFN (gate/up or down) with chunks of
+// rows_r routed and rows_s shared rows.
+template <int K, int NT_S, int NT_R, bool GATEUP, bool XF32>
+static hipError_t launch_stream(FfnArgs a, int rows_r, int rows_s, hipStream_t stream) {
+  const int N = GATEUP ? a.F : a.D;
+  const bool has_s = GATEUP ? a.sg != nullptr : a.sd != nullptr;
+  const int cr = (N + rows_r - 1) / rows_r, cs = has_s ? (N + rows_s - 1) / rows_s : 0;
+  if (GATEUP) {
+    a.rows_gu = rows_r, a.chunks_gu = cr, a.rows_sg = rows_s, a.chunks_sg = cs;
+  } else {
+    a.rows_dn = rows_r, a.chunks_dn = cr, a.rows_sd = rows_s, a.chunks_sd = cs;
   }
-  {  // down
-    const size_t per_row = size_t(2) * a.F * 2 + size_t(a.F / 256) * 64;
-    const size_t fit = (cap - 8320) / per_row;
-    MfmaDecodeCfg c{int(std::max<size_t>(1, std::min<size_t>(size_t(std::min(a.T, 16)), fit))), 2};
-    BM_LAUNCH("ffn_mfma_down_kernel", (ffn_mfma_decode_kernel<false, XF32>), dim3(a.u_max * (a.D / 16)), dim3(256),
-              mfma_decode_smem(a.F, c.np, 2), stream, a, c);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (a.sd && (err = launch_down_gemv<(NT > 2 ? 2 : NT)>(sh, stream)) != hipSuccess) return err;
-  }
-  return hipSuccess;
+  const unsigned grid = unsigned(cs + a.u_max * cr);
+  if (grid == 0) return hipSuccess;
+  BM_LAUNCH(GATEUP ? "ffn_gateup_kernel" : "ffn_down_kernel", (ffn_stream_kernel<K, NT_S, NT_R, GATEUP, XF32>),
+            dim3(grid), dim3(64), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ---- combine ----------------------------------------------------------------
@@ -1071,32 +1103,44 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
 
 // ---- launch -----------------------------------------------------------------
 
-template <int NT_GU, int NT_DN, bool XF32>
+// Token passes: NT_GU / NT_DN for the shared job, NT_R (or one) for routed jobs.
+template <int NT_GU, int NT_DN, int NT_R, bool XF32>
 static hipError_t launch_decode_nt(const FfnArgs &a, hipStream_t stream) {
-  hipError_t err = launch_gateup_gemv<NT_GU, XF32>(a, stream);
+  hipError_t err = launch_gateup_gemv<NT_GU, NT_R, XF32>(a, stream);
   if (err != hipSuccess) return err;
-  return launch_down_gemv<NT_DN>(a, stream);
+  return launch_down_gemv<NT_DN, NT_R>(a, stream);
 }
 
+// Streamed gate/up (K = D) and down (K = F) with NT_S / NT_R token passes.
+template <int D, int F, int NT_S, int NT_R, bool XF32>
+static hipError_t launch_stream_ffn(const FfnArgs &a, hipStream_t stream) {
+  hipError_t err = launch_stream<D, NT_S, NT_R, true, XF32>(a, STREAM_ROWS_GU, STREAM_ROWS_SG, stream);
+  if (err != hipSuccess) return err;
+  return launch_stream<F, NT_S, NT_R, false, XF32>(a, STREAM_ROWS_DN, STREAM_ROWS_SD, stream);
+}
+
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Routed experts and shared expert per launch:
+//  T = 1: the register GEMV kernels (every wave loads its rows' bytes up
+//         front; the one-token code has the fewest instructions per weight);
+//  T >= 2 at d_model 4096, d_ff 2048 (weights 16-byte aligned): the streamed
+//         kernels, routed jobs of one pair on the one-token code;
+//  other shapes: the register GEMV kernels in token passes.
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
-  const bool mfma = a.T >= 3 && a.D % 256 == 0 && a.F % 256 == 0;
   a.u_max = a.T * a.k;  // one job slot per pair; repeated experts exit at once
   hipError_t err;
-  if (mfma) {
-    // routed experts on MFMA, shared expert on the GEMV rows of the same launches
-    if (a.T == 1)
-      err = xf32 ? launch_mfma_decode<1, true>(a, stream) : launch_mfma_decode<1, false>(a, stream);
-    else if (a.T == 2 || xf32)
-      err = xf32 ? launch_mfma_decode<2, true>(a, stream) : launch_mfma_decode<2, false>(a, stream);
-    else
-      err = launch_mfma_decode<NTOK, false>(a, stream);
-  } else if (a.T == 1) {
-    err = xf32 ? launch_decode_nt<1, 1, true>(a, stream) : launch_decode_nt<1, 1, false>(a, stream);
-  } else if (a.T == 2 || xf32) {
-    err = xf32 ? launch_decode_nt<2, 2, true>(a, stream) : launch_decode_nt<2, 2, false>(a, stream);
-  } else {
-    err = launch_decode_nt<NTOK, 2, false>(a, stream);
-  }
+  const bool stream_ok = a.D == 4096 && a.F == 2048 && aligned16(a.wg) && aligned16(a.wu) && aligned16(a.wd) &&
+                         aligned16(a.sg) && aligned16(a.su) && aligned16(a.sd);
+  if (a.T == 1)
+    err = xf32 ? launch_decode_nt<1, 1, 1, true>(a, stream) : launch_decode_nt<1, 1, 1, false>(a, stream);
+  else if (stream_ok)
+    err = xf32 ? launch_stream_ffn<4096, 2048, 2, 2, true>(a, stream)
+               : launch_stream_ffn<4096, 2048, 2, 2, false>(a, stream);
+  else if (a.T == 2 || xf32)
+    err = xf32 ? launch_decode_nt<2, 2, 2, true>(a, stream) : launch_decode_nt<2, 2, 2, false>(a, stream);
+  else
+    err = launch_decode_nt<NTOK, 2, 2, false>(a, stream);
   if (err != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
                         stream);

@@ -59,6 +59,12 @@ struct Q2Raw {
   uint32_t dd;  // d | dmin << 16
 };
 
+// Hands r over as if produced here.  For loads already completed by an
+// explicit s_waitcnt in asm (which the compiler's wait insertion cannot see),
+// this keeps the compiler from waiting again at the first use, where its
+// count would also cover later loads issued from asm.
+BM_DEVICE void q2_settle(Q2Raw &r) { asm volatile("" : "+v"(r.q), "+v"(r.sc), "+v"(r.dd)); }
+
 BM_DEVICE Q2Raw q2_load(const uint8_t *sb, int g) {
   const int h = g >> 1, p = g & 1;
   Q2Raw r;

@@ -239,9 +239,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
       const int src_row = rows[r];
       if (src_row >= 0 && lane < 32) {
         const uint16_t *src = (part ? a.a_lo : a.a) + size_t(src_row) * a.K + kb * KS + 8 * lane;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src),
-                                         (__attribute__((address_space(3))) void *)(dst + (part * BMt + r) * ROWB),
-                                         16, 0, 0);
+        lds_dma16(src, lds_offset(dst + (part * BMt + r) * ROWB));
       }
     }
   };
@@ -263,6 +261,10 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   issue_a(0, 0);
   load_b(0, cur);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) q2_settle(cur[ng][m]);
   __syncthreads();
   const int nsteps = a.K / KS;
   for (int kb = 0; kb < nsteps; ++kb) {
@@ -345,7 +347,10 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) cur[ng][m] = nxt[ng][m];
+      for (int m = 0; m < NM; ++m) {
+        cur[ng][m] = nxt[ng][m];
+        q2_settle(cur[ng][m]);
+      }
   }
   // epilogue: lane holds rows 16 mi + 4 g + r of column n_w + 16 ng
 #pragma unroll
