@@ -87,8 +87,11 @@ def stored_traffic(kernel_src: str, label: str):
     return float(vals["traffic_bytes"])
 
 
-def cpu_baseline(seed: int, n_tokens: int) -> dict:
-    """The fp64 oracle on the host for a bounded sample of decode tokens."""
+def cpu_baseline(seed: int, n_tokens: int, repeats: int) -> dict:
+    """The fp64 oracle on the host for a bounded sample of decode tokens: each
+    token's whole layer is computed `repeats` times on the same inputs (the
+    inputs are generated before timing and the oracle caches nothing, so every
+    repeat does the full work)."""
     import threadpoolctl
 
     import synthdata
@@ -96,22 +99,25 @@ def cpu_baseline(seed: int, n_tokens: int) -> dict:
 
     cfg = synthdata.CONFIGS["decode"]
     ld = synthdata.LayerData(cfg, seed, 0)
+    sh = {kd: ld.shared_bytes(kd) for kd in ("gate", "up", "down")}
     total = 0.0
     for t in range(n_tokens):
         x = ld.x_values(10_000 + t, 1)
         ids, _, _ = moe.route(x, ld.router(), cfg.top_k)
         # the layer's inputs (selected experts' bytes) are generated before timing
         cache = {(kd, int(e)): ld.expert_bytes(kd, int(e)) for e in ids[0] for kd in ("gate", "up", "down")}
-        sh = {kd: ld.shared_bytes(kd) for kd in ("gate", "up", "down")}
         layer = moe.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, ld.router(),
                           lambda kd, e: cache[(kd, e)], lambda kd: sh[kd])
         with threadpoolctl.threadpool_limits(limits=1):  # one core, stated below
-            t0 = time.perf_counter()
-            moe.moe_layer(layer, x)
-            total += time.perf_counter() - t0
-    return {"value": round(n_tokens / total, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} decode tokens of layer instance 0 (whole fp64 layer: router, 6 experts "
-                      f"dequantised + SwiGLU FFN, Q8_0 shared expert, combine) in {total:.1f} s on one core"}
+            for _ in range(repeats):
+                t0 = time.perf_counter()
+                moe.moe_layer(layer, x)
+                total += time.perf_counter() - t0
+    n = n_tokens * repeats
+    return {"value": round(n / total, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens of layer instance 0, each through the whole fp64 layer (router, "
+                      f"6 experts dequantised + SwiGLU FFN, Q8_0 shared expert, combine) {repeats} times: "
+                      f"{n} layer passes in {total:.1f} s on one core"}
 
 
 def make_layer(bm, torch, synthdata, cfg, seed: int, layer: int, lut, dev):
@@ -361,7 +367,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-repeats", type=int, default=6)
     ap.add_argument("--verify-steps", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -473,7 +480,7 @@ def main() -> int:
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens, args.cpu_repeats)
     print(json.dumps(out), flush=True)
     return 0
 
