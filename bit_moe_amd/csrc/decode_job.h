@@ -43,15 +43,16 @@ BM_DEVICE bool pair_job(const FfnArgs &a, int p, Job &job) {
   return true;
 }
 
-// pair_job for a block of one wave: the call's pair ids are read by the lanes
-// (T * k <= 64) and matched with one ballot.
+// pair_job computed by each wave on its own: the call's pair ids are read by
+// the lanes (T * k <= 64) together with the block's own id, and matched with
+// one ballot, so the job costs one round trip to memory.
 BM_DEVICE bool pair_job_wave(const FfnArgs &a, int p, Job &job) {
   const int P = a.T * a.k;
   if (P > 64) return pair_job(a, p, job);
-  const int e = a.ids[p];
-  if (e < 0 || e >= a.E) return false;
   const int lane = threadIdx.x & 63;
   const int id = lane < P ? a.ids[lane] : -1;
+  const int e = __builtin_amdgcn_readlane(id, p);  // ids[p], p < P
+  if (e < 0 || e >= a.E) return false;
   uint64_t m = __ballot(id == e);
   if (m & ((uint64_t(1) << p) - 1)) return false;  // an earlier pair chose e
   job.e = e;

@@ -388,7 +388,7 @@ __global__ void __launch_bounds__(256) ffn_down_kernel(FfnArgs a) {
     nrows = min(a.rows_sd, a.D - r0);
   } else {
     const int b = blockIdx.x - a.chunks_sd;
-    if (!pair_job(a, b / a.chunks_dn, job)) return;
+    if (!pair_job_wave(a, b / a.chunks_dn, job)) return;
     r0 = (b % a.chunks_dn) * a.rows_dn;
     nrows = min(a.rows_dn, a.D - r0);
   }
@@ -672,8 +672,9 @@ BM_DEVICE void gateup_rows(const FfnArgs &a, const Job &job, int t0, int nt, int
   const int n_it = (r_end - r_begin + RPI - 1) / RPI;
   // the wave's row iterations it = wave, wave + 4, ...: the weight loads of up
   // to DEPTH of them are issued before any arithmetic, so their memory
-  // latencies overlap
-  constexpr int DEPTH = IS_Q8 ? 2 : (NT == 1 ? 4 : (NV <= 2 ? 2 : 1));
+  // latencies overlap (two at most, so that the one-token kernel stays within
+  // 128 VGPRs and every block of a decode launch is resident at once)
+  constexpr int DEPTH = IS_Q8 ? 2 : (NT == 1 ? 2 : (NV <= 2 ? 2 : 1));
   for (int it0 = wave; it0 < n_it; it0 += 4 * DEPTH) {
     Raw rg[DEPTH], ru[DEPTH];
 #pragma unroll
@@ -737,7 +738,7 @@ __global__ void __launch_bounds__(256) ffn_gateup_kernel(FfnArgs a) {
     r_end = min(a.F, r_begin + a.rows_sg);
   } else {
     const int b = blockIdx.x - a.chunks_sg;
-    if (!pair_job(a, b / a.chunks_gu, job)) return;
+    if (!pair_job_wave(a, b / a.chunks_gu, job)) return;
     r_begin = (b % a.chunks_gu) * a.rows_gu;
     r_end = min(a.F, r_begin + a.rows_gu);
   }
