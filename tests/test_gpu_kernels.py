@@ -300,6 +300,66 @@ def test_decode_bad_expert_id_skipped_and_recorded():
     assert compare.max_rel_error(y.cpu().numpy(), ref) < 1e-4
 
 
+def _forced_selection_check(ld, ids_h, tag, T):
+    """Experts on a given selection (weights renormalised over it, from the
+    oracle's logits) against the oracle on the same selection."""
+    layer = device_layer(ld)
+    x = x_device(ld, tag, T)
+    xv = ld.x_values(tag, T)
+    _, _, L = moe.route(xv, ld.router(), ld.cfg.top_k)
+    w_h = moe.weights_for_selection(L, ids_h).astype(np.float32)
+    ws = bm.workspace(layer, T, bm.MODE_DECODE)
+    y = bm.expert_ffn(layer, x, torch.from_numpy(ids_h.astype(np.int32)).cuda(), torch.from_numpy(w_h).cuda(), ws,
+                      mode=bm.MODE_DECODE)
+    torch.cuda.synchronize()
+    return y, ws, moe.moe_layer(oracle_layer(ld), xv, ids=ids_h)
+
+
+@pytest.mark.parametrize("T", [2, 5, 8])
+def test_decode_tokens_sharing_experts(T):
+    # every token picks the same six experts (in rotated orders) and one of its
+    # own: jobs of T pairs run in passes of two tokens next to one-pair jobs
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 8)
+    common = np.array([3, 77, 150, 211, 300, 383])
+    ids_h = np.stack([np.roll(common, t) for t in range(T)])
+    ids_h[:, 5] = 10 + 37 * np.arange(T)  # one expert of its own per token
+    y, ws, ref = _forced_selection_check(ld, ids_h, 300 + T, T)
+    err = compare.max_rel_error(y.float().cpu().numpy().astype(np.float64), ref.out)
+    print(f"[parity] shared-expert jobs T={T} max rel err {err:.3e}")
+    assert err < TOL
+    assert bm.read_status(bm.ws_status(ws))[0] == 0
+
+
+def test_decode_streamed_bad_expert_ids():
+    # out-of-range ids at T=5 (streamed kernels): those pairs contribute nothing
+    # and the smallest offending pair index is recorded
+    ld = synthdata.LayerData(synthdata.CONFIGS["verify"], 9)
+    T, k = 5, 6
+    xv = ld.x_values(310, T)
+    r_ids, _, L = moe.route(xv, ld.router(), k)
+    ids_h = r_ids.copy()
+    ids_h[1, 4] = 384
+    ids_h[3, 0] = -1
+    valid = ids_h.clip(0, 383)  # the oracle runs the clipped selection; those two terms are removed below
+    w_h = moe.weights_for_selection(L, valid).astype(np.float32)
+    layer = device_layer(ld)
+    x = x_device(ld, 310, T)
+    ws = bm.workspace(layer, T, bm.MODE_DECODE)
+    y = bm.expert_ffn(layer, x, torch.from_numpy(ids_h.astype(np.int32)).cuda(), torch.from_numpy(w_h).cuda(), ws,
+                      out_dtype=torch.float32, mode=bm.MODE_DECODE)
+    code, detail = bm.read_status(bm.ws_status(ws))
+    assert code == bm.DEV_BAD_EXPERT and detail == 1 * k + 4
+    ol = oracle_layer(ld)
+    ref = moe.moe_layer(ol, xv, ids=valid)
+    y_pairs = moe.expert_outputs(ol, xv, valid)
+    want = ref.out.copy()
+    want[1] -= ref.weights[1, 4] * y_pairs[1, 4]
+    want[3] -= ref.weights[3, 0] * y_pairs[3, 0]
+    err = compare.max_rel_error(y.cpu().numpy().astype(np.float64), want)
+    print(f"[parity] streamed bad ids max rel err {err:.3e}")
+    assert err < 1e-4
+
+
 # ------------------------------------------------------------------ prefill (grouped GEMM)
 
 
