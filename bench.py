@@ -368,7 +368,7 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-tokens", type=int, default=4)
-    ap.add_argument("--cpu-repeats", type=int, default=6)
+    ap.add_argument("--cpu-repeats", type=int, default=25)
     ap.add_argument("--verify-steps", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
