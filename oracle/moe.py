@@ -120,6 +120,55 @@ def weights_for_selection(L: np.ndarray, ids: np.ndarray) -> np.ndarray:
     return ps / ps.sum(axis=1, keepdims=True)
 
 
+# ---------------------------------------------------------------- router variants
+# "Strata-DSV4.1", §Results: decode routes with selection-only biases whose
+# mixing weights stay exact; "DeepSeek-V4-Flash" (what this is): hash routing
+# on the first layers; the commit notes of the DeepSeek-V4-Flash-Vision
+# bias work: a row routed by a table or by a biased learned top-k gathers its
+# weights from the UNBIASED scores, and the scoring there is sqrt(softplus).
+# Readings where the pages stop: the selection bias is added to the score
+# (softmax probability or sqrt-softplus value) of every expert, the top-k of
+# that sum is taken with the tie rule above, and the weights are the unbiased
+# scores of the selected experts divided by their sum (for softmax scores this
+# is the same renormalisation as step 2).
+
+SCORE_SOFTMAX = "softmax"
+SCORE_SQRT_SOFTPLUS = "sqrt_softplus"
+
+
+def softplus(L: np.ndarray) -> np.ndarray:
+    """log(1 + e^L) in float64, written so that large |L| neither overflows nor
+    loses the small term: max(L, 0) + log1p(e^-|L|)."""
+    L = np.asarray(L, dtype=np.float64)
+    return np.maximum(L, 0.0) + np.log1p(np.exp(-np.abs(L)))
+
+
+def route_scores(L: np.ndarray, score: str) -> np.ndarray:
+    """Per-expert routing score of logits L [T][E]."""
+    if score == SCORE_SOFTMAX:
+        return softmax(L)
+    if score == SCORE_SQRT_SOFTPLUS:
+        return np.sqrt(softplus(L))
+    raise ValueError(score)
+
+
+def route_variant(x, w_router, k: int, logit_bias=None, select_bias=None, score: str = SCORE_SOFTMAX,
+                  hash_ids=None):
+    """Routing with the pages' variants.  hash_ids [T][k] (a hash-routed layer:
+    the rows of its token-id table for the tokens) replaces the selection.
+    Returns (ids int64 [T][k], weights float64 [T][k], logits [T][E],
+    selection score [T][E])."""
+    L = router_logits(x, w_router, logit_bias)
+    sc = route_scores(L, score)
+    sel = sc if select_bias is None else sc + np.asarray(select_bias, dtype=np.float64)[None, :]
+    if hash_ids is not None:
+        ids = np.asarray(hash_ids, dtype=np.int64)
+    else:
+        ids = topk_ids(sel, k)
+    g = np.take_along_axis(sc, ids, axis=1)
+    return ids, g / g.sum(axis=1, keepdims=True), L, sel
+
+
 # ---------------------------------------------------------------- plan
 
 
