@@ -274,6 +274,54 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
             "kernels": kernel_table(prof, {}, gemm_flops)}
 
 
+def bench_router_variants(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """moe_route and the moe_route_ex variants (selection-only bias, sqrt-softplus
+    scores, hash-routed rows) at T=1 (HIP graph of K calls over 16 router
+    matrices) and T=4096 (eager)."""
+    cfg = synthdata.CONFIGS["decode"]
+    E, k, D = cfg.n_experts, cfg.top_k, cfg.d_model
+    ld = synthdata.LayerData(cfg, args.seed, 0)
+    base, _ = make_layer(bm, torch, synthdata, cfg, args.seed, 0, lut, dev)
+    NI = 16
+    gen = torch.Generator(device="cpu").manual_seed(args.seed)
+    routers = [(torch.randn((E, D), generator=gen) * 0.02).to(dev) for _ in range(NI)]
+    layers = [bm.Layer(D, cfg.d_ff, E, k, base.w_gate, base.w_up, base.w_down, r, base.ws_gate, base.ws_up,
+                       base.ws_down) for r in routers]
+    sel_b = (torch.randn(E, generator=gen) * (2.0 / E)).to(dev)
+    vocab = 129280
+    table = torch.stack([torch.randperm(E, generator=gen)[:k] for _ in range(1024)]).repeat(vocab // 1024 + 1, 1)
+    table = table[:vocab].to(torch.int32).contiguous().to(dev)
+    variants = {
+        "softmax": {},
+        "softmax_select_bias": {"select_bias": sel_b},
+        "sqrt_softplus_select_bias": {"score": bm.SCORE_SQRT_SOFTPLUS, "select_bias": sel_b},
+        "hash_rows": {"hash_table": table},
+    }
+    out = {}
+    for T, K, graph in ((1, 200, not args.no_graph), (4096, 10, False)):
+        xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 70, T, D).view(np.int16)).to(dev)
+        xs = xs.view(torch.bfloat16).view(T, D)
+        tok = torch.from_numpy(synthdata.token_ids(args.seed, 71, T).astype(np.int32)).to(dev)
+        ws = bm.workspace(layers[0], T)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        for name, kw in variants.items():
+            kw = dict(kw)
+            if "hash_table" in kw:
+                kw["token_ids"] = tok
+
+            def step(i, kw=kw):
+                bm.route_ex(layers[i % NI], xs, ws, ids=ids, weights=wts, **kw)
+
+            g_ms, e_ms, _ = time_steps(bm, torch, step, K, 5, graph)
+            ms = (g_ms if g_ms is not None else e_ms) / K
+            out[f"T{T}_{name}_us"] = round(ms * 1000, 2)
+        del ws
+    out["timing"] = "T=1: one HIP graph of 200 calls; T=4096: 10 eager calls"
+    out["router_bytes_T1"] = E * D * 4
+    return out
+
+
 def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
     """40-layer resident stack: decode T=1 and T=5 (HIP graph) and a prefill
     chunk of T=8192 (eager), each step running every layer (route, experts +
@@ -473,6 +521,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("[bench] prefill workload")
         out["prefill"] = bench_prefill(bm, torch, np, synthdata, args, lut, dev)
+        torch.cuda.empty_cache()
+        log("[bench] router variants")
+        out["router_variants"] = bench_router_variants(bm, torch, np, synthdata, args, lut, dev)
         torch.cuda.empty_cache()
         if not args.no_stack:
             log("[bench] 40-layer stack workload")

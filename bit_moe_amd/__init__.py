@@ -22,11 +22,12 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
 MODE_AUTO, MODE_DECODE, MODE_PREFILL = 0, 1, 2
-DEV_BAD_EXPERT, DEV_BAD_ROW = 1, 2
+DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN = 1, 2, 4
+SCORE_SOFTMAX, SCORE_SQRT_SOFTPLUS = 0, 1
 FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
 
 EXPORTS = [
-    "bitmoe_workspace_size", "moe_route", "moe_expert_ffn", "engram_gather", "moe_plan",
+    "bitmoe_workspace_size", "moe_route", "moe_route_ex", "moe_expert_ffn", "engram_gather", "moe_plan",
     "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
@@ -50,6 +51,13 @@ class _LayerC(ctypes.Structure):
     ]
 
 
+class _RouteOptsC(ctypes.Structure):
+    _fields_ = [
+        ("score", ctypes.c_int32), ("logit_bias", ctypes.c_void_p), ("select_bias", ctypes.c_void_p),
+        ("hash_table", ctypes.c_void_p), ("token_ids", ctypes.c_void_p), ("vocab", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -66,6 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "bitmoe_workspace_size": [LP, I32, I32, ctypes.POINTER(SZ)],
         "moe_route": [LP, P, I32, I32, P, P, P, P, SZ, P],
+        "moe_route_ex": [LP, P, I32, I32, ctypes.POINTER(_RouteOptsC), P, P, P, SZ, P],
         "moe_expert_ffn": [LP, P, I32, I32, P, P, P, I32, I32, P, SZ, P],
         "engram_gather": [P, I64, P, I64, P, P, P],
         "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
@@ -187,6 +196,37 @@ def route(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.
     lc = layer.c()
     _check(lib.moe_route(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids), _ptr(weights),
                          _ptr(ws), ws.numel(), _stream(stream)))
+    return ids, weights
+
+
+def route_ex(layer: Layer, x: torch.Tensor, ws: torch.Tensor, score: int = SCORE_SOFTMAX,
+             logit_bias: Optional[torch.Tensor] = None, select_bias: Optional[torch.Tensor] = None,
+             hash_table: Optional[torch.Tensor] = None, token_ids: Optional[torch.Tensor] = None,
+             ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None, stream=None):
+    """moe_route_ex: router variants (selection-only bias, hash-routed rows,
+    sqrt-softplus scores).  hash_table [vocab][k] int32 with token_ids [T] int32."""
+    lib = load()
+    _require(x, "x")
+    T = x.shape[0]
+    if ids is None:
+        ids = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    _require(ids, "ids", torch.int32)
+    _require(weights, "weights", torch.float32)
+    for t, nm in ((logit_bias, "logit_bias"), (select_bias, "select_bias")):
+        if t is not None:
+            _require(t, nm, torch.float32)
+    vocab = 0
+    if hash_table is not None:
+        _require(hash_table, "hash_table", torch.int32)
+        vocab = hash_table.shape[0]
+    if token_ids is not None:
+        _require(token_ids, "token_ids", torch.int32)
+    o = _RouteOptsC(score, _ptr(logit_bias), _ptr(select_bias), _ptr(hash_table), _ptr(token_ids), vocab)
+    lc = layer.c()
+    _check(lib.moe_route_ex(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, ctypes.byref(o), _ptr(ids),
+                            _ptr(weights), _ptr(ws), ws.numel(), _stream(stream)))
     return ids, weights
 
 

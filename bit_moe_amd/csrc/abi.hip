@@ -242,6 +242,41 @@ int moe_route(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, 
   return BITMOE_OK;
 }
 
+int moe_route_ex(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const bitmoe_route_opts *opts,
+                 int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const char *fn = "moe_route_ex";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (!opts) return fail(BITMOE_EINVAL, "%s: opts is NULL", fn);
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (opts->score != BITMOE_SCORE_SOFTMAX && opts->score != BITMOE_SCORE_SQRT_SOFTPLUS)
+    return fail(BITMOE_EUNSUPPORTED, "%s: score %d", fn, opts->score);
+  if ((opts->hash_table == nullptr) != (opts->token_ids == nullptr))
+    return fail(BITMOE_EINVAL, "%s: hash_table and token_ids go together", fn);
+  if (opts->hash_table && opts->vocab < 1) return fail(BITMOE_EINVAL, "%s: vocab=%lld", fn, (long long)opts->vocab);
+  if (T == 0) return BITMOE_OK;
+  if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(BITMOE_EINVAL, "%s: topk_ids/topk_w NULL or misaligned", fn);
+  const void *opt_ptrs[4] = {opts->logit_bias, opts->select_bias, opts->hash_table, opts->token_ids};
+  for (const void *q : opt_ptrs)
+    if (q && !aligned(q, 4)) return fail(BITMOE_EINVAL, "%s: an option array is misaligned", fn);
+  if (!ws || !aligned(ws, 256)) return fail(BITMOE_EINVAL, "%s: workspace is NULL or not 256-byte aligned", fn);
+  Carve c(ws);
+  int64_t *status;
+  float *logits;
+  carve_common(c, L, T, &status, &logits);
+  if (ws_bytes < c.off)
+    return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, c.off, T);
+  hipError_t e = bm::launch_route_variant(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k,
+                                          L->w_router, opts->logit_bias, opts->score, opts->select_bias,
+                                          opts->hash_table, opts->token_ids, opts->vocab, logits, topk_ids, topk_w,
+                                          status, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
 int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const int32_t *topk_ids,
                    const float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
                    hipStream_t stream) {

@@ -28,6 +28,13 @@ hipError_t launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, i
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr, const float *bias,
                         float *logits, int32_t *ids, float *wts, hipStream_t stream);
 
+// score: 0 softmax, 1 sqrt(softplus); select_bias and hash_table/token_ids
+// optional (see moe_route_ex)
+hipError_t launch_route_variant(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
+                                const float *logit_bias, int score, const float *select_bias,
+                                const int32_t *hash_table, const int32_t *token_ids, int64_t vocab, float *logits,
+                                int32_t *ids, float *wts, int64_t *status, hipStream_t stream);
+
 struct PlanBufs {
   int32_t *counts;
   int32_t *offsets;

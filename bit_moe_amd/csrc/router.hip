@@ -194,6 +194,163 @@ __global__ void __launch_bounds__(256) topk_kernel(const float *__restrict__ log
   topk_token<PER>(logits + int64_t(t) * E, E, k, ids + int64_t(t) * k, wts + int64_t(t) * k, threadIdx.x & 63);
 }
 
+// ---- router variants ----------------------------------------------------------
+// Scores s_e = softmax(L)_e or sqrt(softplus(L_e)); the selection is either
+// the rows of a hash-routed layer's token table or the top-k of s + b (b a
+// selection-only bias; tie -> lower index); the weights are the unbiased
+// scores of the selected experts over their sum.  One wave per token.
+
+// value held in slot `slot` of lane `src` (both wave-uniform)
+template <int PER>
+BM_DEVICE float slot_value(const float (&v)[PER], int src, int slot) {
+  float r = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (i == slot) r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), src));
+  return r;
+}
+
+BM_DEVICE float wave_max_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int PER>
+BM_DEVICE void topk_variant_token(const float *L, int E, int k, int score, const float *sbias, const int32_t *hrow,
+                                  int32_t *ids, float *wts, int64_t *status, int64_t pair0, int lane) {
+  float sc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    sc[i] = e < E ? L[e] : -INFINITY;
+  }
+  if (score == 0) {  // softmax over the E logits
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) m = fmaxf(m, sc[i]);
+    m = wave_max_f(m);
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      sc[i] = lane + 64 * i < E ? __expf(sc[i] - m) : 0.f;
+      z += sc[i];
+    }
+    const float inv = 1.0f / wave_sum(z);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) sc[i] *= inv;
+  } else {  // sqrt(softplus(L)), softplus(v) = max(v, 0) + log1p(e^-|v|)
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      sc[i] = lane + 64 * i < E ? sqrtf(fmaxf(sc[i], 0.f) + log1pf(__expf(-fabsf(sc[i])))) : 0.f;
+  }
+  int sel[8];
+  if (hrow) {
+    for (int j = 0; j < k; ++j) sel[j] = hrow[j];
+  } else {
+    uint32_t key[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      key[i] = e < E ? logit_key(sc[i] + (sbias ? sbias[e] : 0.f)) : 0u;
+    }
+    for (int j = 0; j < k; ++j) {
+      uint32_t mk = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) mk = max(mk, key[i]);
+      const uint32_t M = wave_max_u32(mk);
+      int bi = -1;  // only NaN scores left: no valid expert
+      if (M != 0u) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const uint64_t hit = __ballot(key[i] == M);
+          if (hit) {
+            const int l = __builtin_ctzll(hit);
+            bi = l + 64 * i;
+            if (lane == l) key[i] = 0u;
+            break;
+          }
+        }
+      }
+      sel[j] = bi;
+    }
+  }
+  // unbiased scores of the selection, renormalised
+  float g[8], gs = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int e = sel[j];
+    const bool ok = e >= 0 && e < E;
+    g[j] = ok ? slot_value<PER>(sc, e & 63, e >> 6) : 0.f;
+    gs += g[j];
+    if (!ok && hrow && lane == 0) record_fault(status, 1, pair0 + j);
+  }
+  if (lane == 0) {
+    const float inv = gs > 0.f ? 1.0f / gs : 0.f;
+    for (int j = 0; j < k; ++j) {
+      ids[j] = sel[j];
+      wts[j] = g[j] * inv;
+    }
+  }
+}
+
+template <int PER>
+__global__ void __launch_bounds__(256) topk_variant_kernel(const float *__restrict__ logits, int T, int E, int k,
+                                                           int score, const float *__restrict__ sbias,
+                                                           const int32_t *__restrict__ htab,
+                                                           const int32_t *__restrict__ tok, int64_t vocab,
+                                                           int32_t *__restrict__ ids, float *__restrict__ wts,
+                                                           int64_t *status) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int32_t *hrow = nullptr;
+  if (htab) {
+    const int64_t id = tok[t];
+    if (id < 0 || id >= vocab) {  // no table row: the token routes nowhere
+      if (lane < k) {
+        ids[int64_t(t) * k + lane] = -1;
+        wts[int64_t(t) * k + lane] = 0.f;
+      }
+      if (lane == 0) record_fault(status, 4, t);
+      return;
+    }
+    hrow = htab + id * k;
+  }
+  topk_variant_token<PER>(logits + int64_t(t) * E, E, k, score, sbias, hrow, ids + int64_t(t) * k,
+                          wts + int64_t(t) * k, status, int64_t(t) * k, lane);
+}
+
+hipError_t launch_route_variant(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
+                                const float *logit_bias, int score, const float *select_bias,
+                                const int32_t *hash_table, const int32_t *token_ids, int64_t vocab, float *logits,
+                                int32_t *ids, float *wts, int64_t *status, hipStream_t stream) {
+  if (T <= 8) {
+    if (xbf16)
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr,
+                logit_bias, logits);
+    else
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr,
+                logit_bias, logits);
+  } else {
+    dim3 grid((T + 63) / 64, (E + 63) / 64);
+    if (xbf16)
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr,
+                logit_bias, logits);
+    else
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr,
+                logit_bias, logits);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 grid((T + 3) / 4), block(T == 1 ? 64 : 256);
+  if (E <= 6 * 64)
+    BM_LAUNCH("topk_variant_kernel", topk_variant_kernel<6>, grid, block, 0, stream, logits, T, E, k, score,
+              select_bias, hash_table, token_ids, vocab, ids, wts, status);
+  else
+    BM_LAUNCH("topk_variant_kernel", topk_variant_kernel<16>, grid, block, 0, stream, logits, T, E, k, score,
+              select_bias, hash_table, token_ids, vocab, ids, wts, status);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
                         const float *bias, float *logits, int32_t *ids, float *wts, hipStream_t stream) {
   if (T <= 8) {

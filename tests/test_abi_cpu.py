@@ -96,6 +96,25 @@ def test_route_rejects_bad_args(lib):
     assert lib.moe_route(ctypes.byref(L), None, bm.BF16, -1, None, None, None, None, 0, None) == bm.EINVAL
 
 
+def test_route_ex_rejects_bad_args(lib):
+    L = _layer()
+    P = ctypes.c_void_p
+    f = P(0x10000)
+
+    def call(opts, T=1, x=f, ws_bytes=1 << 30):
+        return lib.moe_route_ex(ctypes.byref(L), x, bm.BF16, T, None if opts is None else ctypes.byref(opts), f, f,
+                                f, ws_bytes, None)
+
+    assert call(None) == bm.EINVAL
+    assert call(bm._RouteOptsC(score=5)) == bm.EUNSUPPORTED
+    assert call(bm._RouteOptsC(hash_table=0x10000)) == bm.EINVAL  # table without token ids
+    assert call(bm._RouteOptsC(hash_table=0x10000, token_ids=0x10000, vocab=0)) == bm.EINVAL
+    assert call(bm._RouteOptsC(select_bias=0x10002)) == bm.EINVAL  # misaligned option array
+    assert call(bm._RouteOptsC(), ws_bytes=64) == bm.EWORKSPACE
+    assert call(bm._RouteOptsC(), x=None) == bm.EINVAL
+    assert call(bm._RouteOptsC(), T=0, x=None) == bm.OK
+
+
 def test_expert_ffn_rejects_bad_args(lib):
     L = _layer()
     P = ctypes.c_void_p
