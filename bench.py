@@ -322,6 +322,49 @@ def bench_router_variants(bm, torch, np, synthdata, args, lut, dev) -> dict:
     return out
 
 
+def engram_inject_bytes(T: int, n_rows: int, W: int) -> dict:
+    """Bytes per launch of the two Engram injection kernels: the projection
+    reads the KV weight and the rows and writes the float32 keys and value; the
+    gate kernel reads those, the two norm weights, and reads and writes the
+    residual branches."""
+    K = n_rows * 256
+    kv = T * 5 * W * 4
+    return {"engram_kv_kernel": 5 * W * K * 2 + T * K * 2 + kv,
+            "engram_gate_kernel": kv + T * 4 * W * 2 * 2 + 2 * 4 * W * 4 + T * 4 * 4}
+
+
+def bench_engram_inject(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """engram_inject at the real model's shape (24 rows per token, width 5120)
+    for T = 1 and 5 (HIP graph of K calls over 2 KV weights, 630 MB in all) and
+    T = 64 (eager)."""
+    n_rows, W = synthdata.ENGRAM_INJECT_ROWS, synthdata.ENGRAM_INJECT_WIDTH
+    K_in = n_rows * 256
+    NI = 2
+    gen = torch.Generator(device=dev).manual_seed(args.seed)
+    w_kv = [(torch.randn((5 * W, K_in), generator=gen, device=dev) / K_in ** 0.5).to(torch.bfloat16)
+            for _ in range(NI)]
+    qn, kn = (torch.from_numpy(a).to(dev) for a in synthdata.engram_branch_norms(args.seed, W))
+    out = {"shape": f"rows [T][{n_rows}][256] bf16, w_kv [{5 * W}][{K_in}] bf16, residual [T][4][{W}] bf16"}
+    for T, K, graph in ((1, 200, not args.no_graph), (5, 200, not args.no_graph), (64, 20, False)):
+        rows = torch.randn((T, n_rows, 256), generator=gen, device=dev).to(torch.bfloat16)
+        res = torch.randn((T, 4, W), generator=gen, device=dev).to(torch.bfloat16)
+        gate = torch.empty((T, 4), dtype=torch.float32, device=dev)
+        n = bm.engram_inject_workspace_bytes(T, W)
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+        def step(i):
+            bm.engram_inject(rows, w_kv[i % NI], qn, kn, 1e-6, res, gate_out=gate, ws=ws)
+
+        g_ms, e_ms, prof = time_steps(bm, torch, step, K, 5, graph)
+        ms = (g_ms if g_ms is not None else e_ms) / K
+        alg = engram_inject_bytes(T, n_rows, W)
+        out[f"T{T}"] = {"us_per_call": round(ms * 1000, 2), "timing": "hip graph" if g_ms is not None else "eager",
+                        "hbm_gbps_call": round(sum(alg.values()) / (ms * 1e-3) / 1e9, 1),
+                        "kernels": kernel_table(prof, alg)}
+        del ws
+    return out
+
+
 def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
     """40-layer resident stack: decode T=1 and T=5 (HIP graph) and a prefill
     chunk of T=8192 (eager), each step running every layer (route, experts +
@@ -524,6 +567,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         log("[bench] router variants")
         out["router_variants"] = bench_router_variants(bm, torch, np, synthdata, args, lut, dev)
+        torch.cuda.empty_cache()
+        log("[bench] engram injection")
+        out["engram_inject"] = bench_engram_inject(bm, torch, np, synthdata, args, lut, dev)
         torch.cuda.empty_cache()
         if not args.no_stack:
             log("[bench] 40-layer stack workload")

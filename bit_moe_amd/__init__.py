@@ -31,7 +31,7 @@ EXPORTS = [
     "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
-    "bitmoe_residual_rescale",
+    "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size",
 ]
 
 
@@ -84,6 +84,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "bitmoe_probe_read": [P, I64, P, I32, P],
         "bitmoe_residual_rescale": [P, P, I32, I32, I32, P, P],
+        "engram_inject_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
+        "engram_inject": [P, I32, I32, P, I32, P, P, ctypes.c_float, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -244,6 +246,35 @@ def expert_ffn(layer: Layer, x: torch.Tensor, ids: torch.Tensor, weights: torch.
     _check(lib.moe_expert_ffn(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(ids), _ptr(weights), _ptr(y),
                               _dtype_code(y), mode, _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def engram_inject_workspace_bytes(T: int, width: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().engram_inject_workspace_size(T, width, ctypes.byref(n)))
+    return max(n.value, 1)
+
+
+def engram_inject(rows: torch.Tensor, w_kv: torch.Tensor, q_norm: torch.Tensor, k_norm: torch.Tensor, eps: float,
+                  residual: torch.Tensor, mask: Optional[torch.Tensor] = None, gate_out: Optional[torch.Tensor] = None,
+                  ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """engram_inject: rows [T][n_rows][256] bf16/int16 bits, w_kv [5W][n_rows*256] bf16,
+    q_norm/k_norm [4][W] float32, residual [T][4][W] bf16 updated in place."""
+    lib = load()
+    T, n_rows = rows.shape[0], rows.shape[1]
+    W = residual.shape[2]
+    for t, nm in ((rows, "rows"), (w_kv, "w_kv"), (residual, "residual")):
+        _require(t, nm)
+    _require(q_norm, "q_norm", torch.float32)
+    _require(k_norm, "k_norm", torch.float32)
+    if mask is not None:
+        _require(mask, "mask", torch.uint8)
+    if gate_out is not None:
+        _require(gate_out, "gate_out", torch.float32)
+    if ws is None:
+        ws = torch.empty(engram_inject_workspace_bytes(T, W), dtype=torch.uint8, device=residual.device)
+    _check(lib.engram_inject(_ptr(rows), T, n_rows, _ptr(w_kv), W, _ptr(q_norm), _ptr(k_norm), float(eps),
+                             _ptr(mask), _ptr(residual), _ptr(gate_out), _ptr(ws), ws.numel(), _stream(stream)))
+    return residual
 
 
 def engram_gather(table: torch.Tensor, row_ids: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -362,6 +362,39 @@ int engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, 
   return BITMOE_OK;
 }
 
+int engram_inject_workspace_size(int32_t T, int32_t width, size_t *bytes) {
+  if (!bytes || T < 0 || width < 256 || width > 8192 || width % 256)
+    return fail(BITMOE_EINVAL, "engram_inject_workspace_size: bad arguments (T=%d width=%d)", T, width);
+  *bytes = up256(size_t(T) * 5 * width * sizeof(float));
+  return BITMOE_OK;
+}
+
+int engram_inject(const uint16_t *rows, int32_t T, int32_t n_rows, const uint16_t *w_kv, int32_t width,
+                  const float *q_norm, const float *k_norm, float eps, const uint8_t *mask, uint16_t *residual,
+                  float *gate_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  const char *fn = "engram_inject";
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (T > 262144) return fail(BITMOE_EUNSUPPORTED, "%s: T=%d above 262144 positions per call", fn, T);
+  if (n_rows < 2 || n_rows > 32 || n_rows % 2)
+    return fail(BITMOE_EUNSUPPORTED, "%s: n_rows=%d must be even in [2, 32]", fn, n_rows);
+  if (width < 256 || width > 8192 || width % 256)
+    return fail(BITMOE_EUNSUPPORTED, "%s: width=%d must be a multiple of 256 in [256, 8192]", fn, width);
+  if (!(eps >= 0.f) || eps > 1.f) return fail(BITMOE_EINVAL, "%s: eps=%g", fn, double(eps));
+  if (T == 0) return BITMOE_OK;
+  if (!rows || !w_kv || !residual || !aligned(rows, 16) || !aligned(w_kv, 16) || !aligned(residual, 16))
+    return fail(BITMOE_EINVAL, "%s: rows, w_kv or residual NULL or not 16-byte aligned", fn);
+  if (!q_norm || !k_norm || !aligned(q_norm, 16) || !aligned(k_norm, 16) || (gate_out && !aligned(gate_out, 4)))
+    return fail(BITMOE_EINVAL, "%s: q_norm/k_norm NULL or not 16-byte aligned, or gate_out misaligned", fn);
+  size_t need = 0;
+  engram_inject_workspace_size(T, width, &need);
+  if (!ws || !aligned(ws, 256)) return fail(BITMOE_EINVAL, "%s: workspace is NULL or not 256-byte aligned", fn);
+  if (ws_bytes < need) return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, ws_bytes, need);
+  hipError_t e = bm::launch_engram_inject(rows, T, n_rows, w_kv, width, q_norm, k_norm, eps, mask, residual, gate_out,
+                                          static_cast<float *>(ws), stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
 int bitmoe_plan_workspace_size(int32_t T, int32_t k, int32_t n_experts, size_t *bytes) {
   if (!bytes || T < 0 || k < 1 || n_experts < 1 || n_experts > 1024)
     return fail(BITMOE_EINVAL, "bitmoe_plan_workspace_size: bad arguments (T=%d k=%d E=%d)", T, k, n_experts);

@@ -20,6 +20,10 @@ void prof_end(hipStream_t stream);
 
 hipError_t launch_engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n,
                                 uint16_t *out, int64_t *status, hipStream_t stream);
+// kv: [T][5 W] float32 scratch
+hipError_t launch_engram_inject(const uint16_t *rows, int T, int n_rows, const uint16_t *w_kv, int W,
+                                const float *q_norm, const float *k_norm, float eps, const uint8_t *mask,
+                                uint16_t *residual, float *gate_out, float *kv, hipStream_t stream);
 hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void *out, int out_bf16,
                           hipStream_t stream);
 hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const uint16_t *lut,

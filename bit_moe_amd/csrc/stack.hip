@@ -15,21 +15,6 @@
 
 namespace bm {
 
-// bf16 bits of a float64 value, rounded to nearest-even once: the float32
-// conversion (RNE) is exact to 29 extra bits, so it only misleads the second
-// rounding when it lands on a bf16 halfway point; then the float64 value
-// decides the direction.
-BM_DEVICE uint16_t bf16_from_f64(double v) {
-  const float f = float(v);
-  const uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u) return uint16_t((b >> 16) | ((b & 0x007FFFFFu) ? 0x0040u : 0u));
-  if ((b & 0xFFFFu) == 0x8000u && double(f) != v) {
-    const bool away = fabs(v) > fabs(double(f));  // the true value lies beyond the halfway point
-    return uint16_t((b >> 16) + (away ? 1u : 0u));
-  }
-  return f32_to_bf16(f);
-}
-
 // Thread i of the block owns the 16 consecutive elements 16 i .. 16 i + 15 of
 // the row (D / 16 <= 256 threads busy): 16-byte loads and stores.
 template <bool Y_F32>

@@ -147,9 +147,10 @@ def rng(seed: int, *tags: int) -> np.random.Generator:
 
 
 def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
-    """float32 -> BF16 bits, round to nearest even (finite inputs)."""
-    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    """float32 -> BF16 bits, round to nearest even (finite inputs: their bit
+    patterns stay below 0xFF800000, so the sum fits in 32 bits)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -214,6 +215,30 @@ def engram_row_ids(seed: int, tokens: np.ndarray, first: int, n_tables: int = 2,
                 h ^= h >> 32
                 out[t, tb, j] = h % ENGRAM_ROWS
     return out
+
+
+# Engram injection inputs (the layer's KV weight, branch norm weights, residual
+# branches).  The real model's shape: 24 gathered rows per token, width 5120.
+ENGRAM_INJECT_ROWS, ENGRAM_INJECT_WIDTH = 24, 5120
+
+
+def engram_kv_weight(seed: int, n_rows: int, width: int, scale: float = 1.0) -> np.ndarray:
+    """BF16 bits [5 width][n_rows 256]: N(0, 1) * scale / sqrt(n_rows 256)."""
+    K = n_rows * 256
+    g = rng(seed, 80, n_rows, width)
+    w = g.standard_normal((5 * width, K), dtype=np.float32) * np.float32(scale / np.sqrt(K))
+    return bf16_bits_from_f32(w)
+
+
+def engram_branch_norms(seed: int, width: int):
+    """q_norm, k_norm float32 [4][width]: 1 + 0.1 N(0, 1)."""
+    g = rng(seed, 81, width)
+    return (1.0 + 0.1 * g.standard_normal((2, 4, width))).astype(np.float32)
+
+
+def residual_branches(seed: int, T: int, width: int) -> np.ndarray:
+    """BF16 bits [T][4][width], N(0, 1)."""
+    return bf16_bits_from_f32(rng(seed, 82, T, width).standard_normal((T, 4, width), dtype=np.float32))
 
 
 # ---------------------------------------------------------------- configurations

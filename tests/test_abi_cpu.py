@@ -115,6 +115,27 @@ def test_route_ex_rejects_bad_args(lib):
     assert call(bm._RouteOptsC(), T=0, x=None) == bm.OK
 
 
+def test_engram_inject_rejects_bad_args(lib):
+    f = ctypes.c_void_p(0x10000)
+    n = ctypes.c_size_t(0)
+    assert lib.engram_inject_workspace_size(5, 4096, ctypes.byref(n)) == bm.OK and n.value >= 5 * 5 * 4096 * 4
+    assert lib.engram_inject_workspace_size(5, 300, ctypes.byref(n)) == bm.EINVAL
+
+    def call(T=5, n_rows=8, W=4096, eps=1e-6, rows=f, qn=f, ws_bytes=1 << 30):
+        return lib.engram_inject(rows, T, n_rows, f, W, qn, f, ctypes.c_float(eps), None, f, None, f, ws_bytes, None)
+
+    assert call(n_rows=7) == bm.EUNSUPPORTED
+    assert call(n_rows=34) == bm.EUNSUPPORTED
+    assert call(W=4000) == bm.EUNSUPPORTED
+    assert call(eps=-1.0) == bm.EINVAL
+    assert call(rows=None) == bm.EINVAL
+    assert call(rows=ctypes.c_void_p(0x10008)) == bm.EINVAL
+    assert call(qn=ctypes.c_void_p(0x10004)) == bm.EINVAL  # the norm weights are read 16 bytes at a time
+    assert call(ws_bytes=1024) == bm.EWORKSPACE
+    assert call(T=0, rows=None) == bm.OK
+    assert call(T=-1) == bm.EINVAL
+
+
 def test_expert_ffn_rejects_bad_args(lib):
     L = _layer()
     P = ctypes.c_void_p
