@@ -459,13 +459,15 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-tokens", type=int, default=4)
-    ap.add_argument("--cpu-repeats", type=int, default=25)
+    ap.add_argument("--cpu-repeats", type=int, default=60)
     ap.add_argument("--verify-steps", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the verify, prefill and stack workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip every workload beside the decode line")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack workload")
+    ap.add_argument("--only", nargs="+", choices=["verify", "prefill", "router_variants", "engram_inject", "stack"],
+                    help="run only these of the workloads beside the decode line")
     ap.add_argument("--stack-prefill-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 plain device-to-device copies of MIB MiB (reference kernel for the "
@@ -558,23 +560,14 @@ def main() -> int:
         "eager_ms_per_step": round(eager_ms / K, 5),
         "kernels": kernel_table(prof, alg),
     }
-    if not args.no_extra:
-        log("[bench] verify workload")
-        out["verify"] = bench_verify(bm, torch, np, synthdata, args, lut, dev)
+    extras = (("verify", bench_verify), ("prefill", bench_prefill), ("router_variants", bench_router_variants),
+              ("engram_inject", bench_engram_inject), ("stack", bench_stack))
+    for name, fn in extras:
+        if args.no_extra or (args.only and name not in args.only) or (name == "stack" and args.no_stack):
+            continue
+        log(f"[bench] {name} workload")
+        out[name] = fn(bm, torch, np, synthdata, args, lut, dev)
         torch.cuda.empty_cache()
-        log("[bench] prefill workload")
-        out["prefill"] = bench_prefill(bm, torch, np, synthdata, args, lut, dev)
-        torch.cuda.empty_cache()
-        log("[bench] router variants")
-        out["router_variants"] = bench_router_variants(bm, torch, np, synthdata, args, lut, dev)
-        torch.cuda.empty_cache()
-        log("[bench] engram injection")
-        out["engram_inject"] = bench_engram_inject(bm, torch, np, synthdata, args, lut, dev)
-        torch.cuda.empty_cache()
-        if not args.no_stack:
-            log("[bench] 40-layer stack workload")
-            out["stack"] = bench_stack(bm, torch, np, synthdata, args, lut, dev)
-            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens, args.cpu_repeats)
