@@ -29,6 +29,7 @@ formats  -- Q2 super-block / Q8_0 dequantisation, E4M3, E8M0, BF16 rounding
 moe      -- router, top-k, plan, expert FFN, combine, brute-force dense MoE
 engram   -- Engram row decode (gather)
 engram_inject -- Engram KV projection and gated injection into the residual branches
+int8_mode -- int8 activation numerics of the expert FFN (block quantiser, integer row dots)
 compare  -- parity comparators (tie-aware ids, tolerance, NaN = failure)
 
 Parity status per function is stated in its docstring; every function here is
