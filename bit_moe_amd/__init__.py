@@ -21,14 +21,14 @@ LIB_PATH = os.path.join(HERE, "libbitmoe.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
-MODE_AUTO, MODE_DECODE, MODE_PREFILL = 0, 1, 2
+MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_DECODE_INT8 = 0, 1, 2, 3
 DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN = 1, 2, 4
 SCORE_SOFTMAX, SCORE_SQRT_SOFTPLUS = 0, 1
 FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
 
 EXPORTS = [
     "bitmoe_workspace_size", "moe_route", "moe_route_ex", "moe_expert_ffn", "engram_gather", "moe_plan",
-    "bitmoe_plan_workspace_size", "moe_dequant", "bitmoe_fill", "bitmoe_read_status",
+    "bitmoe_plan_workspace_size", "moe_dequant", "moe_quantize_q8_1", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
     "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size",
@@ -80,6 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "bitmoe_plan_workspace_size": [I32, I32, I32, ctypes.POINTER(SZ)],
         "moe_dequant": [P, I32, I64, P, I32, P],
+        "moe_quantize_q8_1": [P, I32, I64, I32, P, P, P, P],
         "bitmoe_fill": [P, I64, ctypes.c_uint64, I32, P, P],
         "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "bitmoe_probe_read": [P, I64, P, I32, P],
@@ -319,6 +320,22 @@ def dequant(blocks: torch.Tensor, wfmt: int, n_weights: int, out_dtype=torch.flo
     out = torch.empty(n_weights, dtype=out_dtype, device=blocks.device)
     _check(lib.moe_dequant(_ptr(blocks), wfmt, n_weights, _ptr(out), _dtype_code(out), _stream(stream)))
     return out
+
+
+def quantize_q8_1(x: torch.Tensor, stream=None):
+    """The int8 mode's activation quantiser over a [rows][cols] float32 or bf16
+    tensor -> (q int8 [rows][cols], d float32 [rows][cols/32], s float32
+    [rows][cols/16])."""
+    lib = load()
+    _require(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows][cols]")
+    rows, cols = x.shape
+    q = torch.empty(rows, cols, dtype=torch.int8, device=x.device)
+    d = torch.empty(rows, max(cols // 32, 1), dtype=torch.float32, device=x.device)
+    s = torch.empty(rows, max(cols // 16, 1), dtype=torch.float32, device=x.device)
+    _check(lib.moe_quantize_q8_1(_ptr(x), _dtype_code(x), rows, cols, _ptr(q), _ptr(d), _ptr(s), _stream(stream)))
+    return q, d, s
 
 
 def fill(dst: torch.Tensor, key: int, kind: int, lut: Optional[torch.Tensor] = None, stream=None):

@@ -106,11 +106,23 @@ void carve_decode(Carve &c, const bitmoe_layer *L, int T, DecodeWs *w) {
   w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
 }
 
+// int8 numerics: h in float32 (the quantiser's input) instead of bf16 parts
+void carve_decode_i8(Carve &c, const bitmoe_layer *L, int T, DecodeWs *w, float **hf, float **hsf) {
+  const size_t P = size_t(T) * L->top_k;
+  *hf = static_cast<float *>(c.take(P * L->d_ff * 4));
+  *hsf = static_cast<float *>(c.take(size_t(T) * L->d_ff * 4));
+  w->h = w->hs = w->h_lo = w->hs_lo = nullptr;
+  w->y = static_cast<float *>(c.take(P * L->d_model * 4));
+  w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
+}
+
 // Decode-path kernel arguments over the workspace carve (after the common region).
 bm::FfnArgs decode_args(Carve &c, const bitmoe_layer *L, const void *x, int T, const int32_t *ids, const float *wts,
-                        void *y, int y_dtype, int64_t *status) {
+                        void *y, int y_dtype, int64_t *status, bool int8 = false) {
   DecodeWs w;
-  carve_decode(c, L, T, &w);
+  float *hf = nullptr, *hsf = nullptr;
+  if (int8) carve_decode_i8(c, L, T, &w, &hf, &hsf);
+  else carve_decode(c, L, T, &w);
   const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
   bm::FfnArgs a{};
   a.D = L->d_model;
@@ -131,6 +143,8 @@ bm::FfnArgs decode_args(Carve &c, const bitmoe_layer *L, const void *x, int T, c
   a.hs = w.hs;
   a.h_lo = w.h_lo;
   a.hs_lo = w.hs_lo;
+  a.hf = hf;
+  a.hsf = hsf;
   a.y = w.y;
   a.ys = w.ys;
   a.out = y;
@@ -167,9 +181,14 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
 size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
   Carve c(nullptr);
   carve_common(c, L, T, nullptr, nullptr);
-  if (resolve_mode(mode, T) == BITMOE_MODE_DECODE) {
+  const int m = resolve_mode(mode, T);
+  if (m == BITMOE_MODE_DECODE) {
     DecodeWs w;
     carve_decode(c, L, T, &w);
+  } else if (m == BITMOE_MODE_DECODE_INT8) {
+    DecodeWs w;
+    float *hf, *hsf;
+    carve_decode_i8(c, L, T, &w, &hf, &hsf);
   } else {
     PrefillWs w;
     carve_prefill(c, L, T, &w);
@@ -208,7 +227,7 @@ int bitmoe_workspace_size(const bitmoe_layer *L, int32_t T, int32_t mode, size_t
   if (rc) return rc;
   if (!bytes) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: bytes is NULL");
   if (T < 0) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: T=%d is negative", T);
-  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL)
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_DECODE_INT8)
     return fail(BITMOE_EINVAL, "bitmoe_workspace_size: unknown mode %d", mode);
   *bytes = ws_bytes_for(L, T, mode);
   return BITMOE_OK;
@@ -286,10 +305,13 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
   if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
   if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
-  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL) return fail(BITMOE_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_DECODE_INT8)
+    return fail(BITMOE_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (mode == BITMOE_MODE_DECODE_INT8 && L->d_ff < 256)
+    return fail(BITMOE_EUNSUPPORTED, "%s: int8 numerics need d_ff >= 256 (got %d)", fn, L->d_ff);
   if (T == 0) return BITMOE_OK;
   const int m = resolve_mode(mode, T);
-  if (m == BITMOE_MODE_DECODE && T > MAX_DECODE_T)
+  if ((m == BITMOE_MODE_DECODE || m == BITMOE_MODE_DECODE_INT8) && T > MAX_DECODE_T)
     return fail(BITMOE_EUNSUPPORTED, "%s: decode mode takes at most %d tokens, got T=%d", fn, MAX_DECODE_T, T);
   if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
   if (!y || !aligned(y, 16)) return fail(BITMOE_EINVAL, "%s: y is NULL or not 16-byte aligned", fn);
@@ -304,6 +326,12 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   if (m == BITMOE_MODE_DECODE) {
     const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
     hipError_t e = bm::launch_decode_ffn(a, x_dtype == BITMOE_F32, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return BITMOE_OK;
+  }
+  if (m == BITMOE_MODE_DECODE_INT8) {
+    const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status, true);
+    hipError_t e = bm::launch_decode_ffn_i8(a, x_dtype == BITMOE_F32, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
     return BITMOE_OK;
   }
@@ -431,6 +459,22 @@ int moe_dequant(const void *blocks, int32_t wfmt, int64_t n_weights, void *out, 
   if (!blocks || !aligned(blocks, 4) || !out || !aligned(out, 16))
     return fail(BITMOE_EINVAL, "%s: NULL or misaligned pointer", fn);
   hipError_t e = bm::launch_dequant(blocks, wfmt, n_weights, out, out_dtype == BITMOE_BF16, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int moe_quantize_q8_1(const void *x, int32_t x_dtype, int64_t rows, int32_t cols, int8_t *q, float *d, float *s,
+                      hipStream_t stream) {
+  const char *fn = "moe_quantize_q8_1";
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (rows < 0 || cols <= 0 || cols % 32)
+    return fail(BITMOE_EINVAL, "%s: rows %lld / cols %d (cols must be a positive multiple of 32)", fn,
+                (long long)rows, cols);
+  if (rows == 0) return BITMOE_OK;
+  if (!x || !aligned(x, 16) || !q || !aligned(q, 16) || !d || !aligned(d, 4) || !s || !aligned(s, 4))
+    return fail(BITMOE_EINVAL, "%s: NULL or misaligned pointer", fn);
+  hipError_t e = bm::launch_quantize_q8(x, x_dtype == BITMOE_F32, rows, cols, reinterpret_cast<uint8_t *>(q), d, s,
+                                        stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }

@@ -65,6 +65,8 @@ struct FfnArgs {
   uint16_t *hs;    // [T][F]
   uint16_t *h_lo;  // float32 mode: lo parts, else unused
   uint16_t *hs_lo;
+  float *hf;       // int8 numerics: [T*k][F] float32 h (pair order)
+  float *hsf;      // int8 numerics: [T][F] float32 h of the shared expert
   float *y;
   float *ys;
   void *out;
@@ -77,6 +79,12 @@ struct FfnArgs {
   int u_max;
 };
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream);
+// int8 activation numerics (T <= 8; d_model, d_ff multiples of 256): a.hf /
+// a.hsf carry h, a.h* are unused
+hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream);
+// the int8 mode's quantiser over [rows][cols] (cols a multiple of 32)
+hipError_t launch_quantize_q8(const void *x, bool xf32, int64_t rows, int cols, uint8_t *q, float *d, float *s,
+                              hipStream_t stream);
 hipError_t launch_combine(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k, int D,
                           int E, void *out, int out_bf16, int64_t *status, hipStream_t stream);
 

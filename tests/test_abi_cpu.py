@@ -148,7 +148,38 @@ def test_expert_ffn_rejects_bad_args(lib):
     assert lib.moe_expert_ffn(*args(wsb=64)) == bm.EWORKSPACE
     assert lib.moe_expert_ffn(*args(ws=P(0x10010), wsb=1 << 40)) == bm.EINVAL  # not 256-aligned
     assert lib.moe_expert_ffn(*args(T=9, mode=bm.MODE_DECODE, wsb=1 << 40)) == bm.EUNSUPPORTED
+    assert lib.moe_expert_ffn(*args(T=9, mode=bm.MODE_DECODE_INT8, wsb=1 << 40)) == bm.EUNSUPPORTED
+    assert lib.moe_expert_ffn(*args(mode=4, wsb=1 << 40)) == bm.EINVAL
+    assert lib.moe_expert_ffn(*args(mode=bm.MODE_DECODE_INT8, wsb=64)) == bm.EWORKSPACE
     assert lib.moe_expert_ffn(*args(T=0, x=None, y=None)) == bm.OK
+
+
+def test_int8_mode_workspace_and_shape_limits(lib):
+    L = _layer()
+    n8, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, bm.MODE_DECODE_INT8, ctypes.byref(n8)) == bm.OK
+    assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, bm.MODE_DECODE, ctypes.byref(n1)) == bm.OK
+    # float32 h in place of its two bf16 parts: the same size
+    assert n8.value == n1.value
+    assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, 4, ctypes.byref(n8)) == bm.EINVAL
+    # the int8 mode needs d_ff >= 256 (two 16-value halves per 32-value block of h, whole super-blocks per row)
+    Ls = _layer(d_ff=128)
+    P = ctypes.c_void_p
+    f = P(0x10000)
+    assert lib.moe_expert_ffn(ctypes.byref(Ls), f, bm.BF16, 1, f, f, f, bm.BF16, bm.MODE_DECODE_INT8, f, 1 << 40,
+                              None) == bm.EUNSUPPORTED
+
+
+def test_quantize_rejects_bad_args(lib):
+    P = ctypes.c_void_p
+    f = P(0x10000)
+    assert lib.moe_quantize_q8_1(f, bm.BF16, 4, 48, f, f, f, None) == bm.EINVAL  # cols not a multiple of 32
+    assert lib.moe_quantize_q8_1(f, bm.BF16, 4, 0, f, f, f, None) == bm.EINVAL
+    assert lib.moe_quantize_q8_1(f, 7, 4, 64, f, f, f, None) == bm.EUNSUPPORTED
+    assert lib.moe_quantize_q8_1(None, bm.BF16, 4, 64, f, f, f, None) == bm.EINVAL
+    assert lib.moe_quantize_q8_1(f, bm.BF16, 4, 64, P(0x10004), f, f, None) == bm.EINVAL  # q misaligned
+    assert lib.moe_quantize_q8_1(f, bm.F32, -1, 64, f, f, f, None) == bm.EINVAL
+    assert lib.moe_quantize_q8_1(None, bm.F32, 0, 64, None, None, None, None) == bm.OK
 
 
 def test_engram_gather_rejects_bad_args(lib):

@@ -1,0 +1,165 @@
+"""GPU parity of the int8 activation numerics (BITMOE_MODE_DECODE_INT8)
+against oracle.int8_mode: the quantiser bit for bit on identical inputs, and
+whole decode layers within a tolerance derived below.
+
+Tolerance.  Both sides quantise x identically (same float32 decisions), and
+the integer sub-block sums are exact on both; they differ in the float32
+combination on the device (relative ~1e-6 on g, u and h) against float64 in
+the oracle.  That perturbation can move an element of h across a rounding
+boundary of its quantiser, changing one int8 code of h by one: the down
+output then moves by d_h |w| <= (max|h| / 127) |w| for that column, which
+against an output of ~sqrt(d_ff) rms(h) |w| is below 1e-3 of the token's rms
+for the synthetic layers (max|h| / rms(h) < 6 over a block of 32).  A handful
+of such flips per call stays below TOL_F32; bf16 outputs add their own
+rounding (2^-9 relative)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_moe_amd as bm
+import synthdata
+from oracle import compare, int8_mode, moe
+
+from gpu_util import device_layer, oracle_layer, x_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 5e-3
+TOL_BF16 = 1e-2
+
+SMALL = synthdata.Config("int8-small", 8, 512, 256, 16, 2, "bf16", True)
+SMALL_F32 = synthdata.Config("int8-small-f32", 8, 512, 256, 16, 2, "f32", True)
+
+
+def _quant_check(x_np: np.ndarray, x_dev: torch.Tensor):
+    q, d, s = bm.quantize_q8_1(x_dev)
+    torch.cuda.synchronize()
+    rq, rd, rs = int8_mode.quantize_blocks(x_np)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), rd.view(np.uint32))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_quantizer_bit_exact_f32():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((64, 4096)) * rng.uniform(1e-3, 1e3, (64, 1))).astype(np.float32)
+    x[3, 64:96] = 0.0                            # a zero block
+    x[5, 0:32] = 0.0
+    x[5, 0] = 127.0                              # d = 1 exactly: halves round to even
+    x[5, 1:9] = [2.5, 3.5, -2.5, 0.5, 1.5, -0.5, 126.5, -125.5]
+    x[6, 32:64] = -1e-30                         # tiny values
+    x[7, :] = rng.integers(-127, 128, 4096).astype(np.float32) * np.float32(0.5)  # many exact halves
+    _quant_check(x, torch.from_numpy(x).cuda())
+
+
+def test_quantizer_bit_exact_bf16_and_ragged_rows():
+    for rows, cols in ((1, 32), (3, 96), (17, 4096), (5, 2048)):
+        bits = synthdata.activations_bf16(2, rows * 1000 + cols, rows, cols)
+        x_np = synthdata.bf16_bits_to_f32(bits)
+        x_dev = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        _quant_check(x_np, x_dev)
+
+
+def _int8_layer(ld, T, tag, out_dtype, ids_override=None):
+    cfg = ld.cfg
+    layer = device_layer(ld, host_bytes=cfg.n_experts * ld.blocks_per_expert < 200000)
+    x = x_device(ld, tag, T)
+    ws = bm.workspace(layer, T, bm.MODE_DECODE_INT8)
+    ids, w = bm.route(layer, x, ws)
+    xv = ld.x_values(tag, T)
+    if ids_override is not None:
+        _, _, L = moe.route(xv, ld.router(), cfg.top_k)
+        ids = torch.from_numpy(ids_override.astype(np.int32)).cuda()
+        w = torch.from_numpy(moe.weights_for_selection(L, ids_override).astype(np.float32)).cuda()
+    y = bm.expert_ffn(layer, x, ids, w, ws, out_dtype=out_dtype, mode=bm.MODE_DECODE_INT8)
+    torch.cuda.synchronize()
+    ids_h = ids.cpu().numpy()
+    ref = int8_mode.moe_layer_int8(oracle_layer(ld), xv, ids=ids_h)
+    if ids_override is None:
+        r_ids, _, L = moe.route(xv, ld.router(), cfg.top_k)
+        assert not compare.compare_ids(ids_h, r_ids, L)[2]
+    yv = y.float().cpu().numpy().astype(np.float64)
+    err = compare.max_rel_error(yv, ref.out)
+    print(f"[parity] int8 {cfg.name} T={T} out={out_dtype} max rel err {err:.3e} "
+          f"normwise {compare.normwise_rel_error(yv, ref.out):.3e}")
+    assert bm.read_status(bm.ws_status(ws))[0] == 0
+    return err, y, ref
+
+
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_int8_small_layer(T):
+    ld = synthdata.LayerData(SMALL, 21)
+    err, _, _ = _int8_layer(ld, T, 40 + T, torch.float32)
+    assert err < TOL_F32
+
+
+def test_int8_small_layer_f32_activations():
+    ld = synthdata.LayerData(SMALL_F32, 22)
+    err, _, _ = _int8_layer(ld, 5, 7, torch.float32)
+    assert err < TOL_F32
+
+
+@pytest.mark.parametrize("T", [1, 5])
+def test_int8_full_decode_layer(T):
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 4)
+    err, _, _ = _int8_layer(ld, T, 500 + T, torch.bfloat16)
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("T", [5, 8])
+def test_int8_tokens_sharing_experts(T):
+    # every token picks the same five experts (rotated) and one of its own:
+    # routed jobs of T pairs run in passes of four and two tokens
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 8)
+    common = np.array([3, 77, 150, 211, 300, 383])
+    ids_h = np.stack([np.roll(common, t) for t in range(T)])
+    ids_h[:, 5] = 10 + 37 * np.arange(T)
+    err, _, _ = _int8_layer(ld, T, 700 + T, torch.float32, ids_override=ids_h)
+    assert err < TOL_F32
+
+
+def test_int8_differs_from_float_path_within_quantisation():
+    # the int8 mode really quantises: its outputs move against the float64
+    # layer by more than float32 rounding, and by no more than the few per
+    # cent the oracle's own int8 layer moves
+    ld = synthdata.LayerData(SMALL, 23)
+    _, y, ref8 = _int8_layer(ld, 8, 3, torch.float32)
+    xv = ld.x_values(3, 8)
+    ref = moe.moe_layer(oracle_layer(ld), xv, ids=ref8.ids)
+    e_dev = compare.normwise_rel_error(y.cpu().numpy().astype(np.float64), ref.out)
+    e_orc = compare.normwise_rel_error(ref8.out, ref.out)
+    print(f"[int8] normwise vs float64 layer: device {e_dev:.3e}, oracle int8 {e_orc:.3e}")
+    assert 1e-4 < e_dev < 3e-2
+    assert abs(e_dev - e_orc) < 0.25 * e_orc
+
+
+def test_int8_bad_expert_id_skipped_and_recorded():
+    ld = synthdata.LayerData(SMALL, 24)
+    layer = device_layer(ld, host_bytes=True)
+    x = x_device(ld, 1, 4)
+    ws = bm.workspace(layer, 4, bm.MODE_DECODE_INT8)
+    ids, w = bm.route(layer, x, ws)
+    ids_bad = ids.clone()
+    ids_bad[1, 0] = 99
+    y = bm.expert_ffn(layer, x, ids_bad, w, ws, out_dtype=torch.float32, mode=bm.MODE_DECODE_INT8)
+    code, detail = bm.read_status(bm.ws_status(ws))
+    assert code == bm.DEV_BAD_EXPERT and detail == 1 * 2 + 0
+    ids_h = ids.cpu().numpy()
+    xv = ld.x_values(1, 4)
+    ol = oracle_layer(ld)
+    res = int8_mode.moe_layer_int8(ol, xv, ids=ids_h)
+    y_bad = int8_mode.ffn_int8(ol, int(ids_h[1, 0]), xv[1])[0]
+    ref = res.out.copy()
+    ref[1] -= res.weights[1, 0] * y_bad
+    assert compare.max_rel_error(y.cpu().numpy().astype(np.float64), ref) < TOL_F32
+
+
+def test_int8_deterministic():
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 5)
+    layer = device_layer(ld)
+    x = x_device(ld, 9, 5)
+    ws = bm.workspace(layer, 5, bm.MODE_DECODE_INT8)
+    ids, w = bm.route(layer, x, ws)
+    y1 = bm.expert_ffn(layer, x, ids, w, ws, mode=bm.MODE_DECODE_INT8).clone()
+    y2 = bm.expert_ffn(layer, x, ids, w, ws, mode=bm.MODE_DECODE_INT8)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
