@@ -237,6 +237,52 @@ def bench_verify(bm, torch, np, synthdata, args, lut, dev) -> dict:
             "eager_ms_per_step": round(eager_ms / K, 5), "kernels": kernel_table(prof, alg)}
 
 
+def bench_int8_decode(bm, torch, np, synthdata, args, lut, dev) -> dict:
+    """The decode layer in int8 activation numerics (moe_expert_ffn mode
+    DECODE_INT8) at T=1 (as the decode line) and T=5 (a verify batch without
+    the Engram gathers), HIP-graph replay over the same 16 layer instances."""
+    cfg = synthdata.CONFIGS["decode"]
+    NI = args.instances
+    layers = [make_layer(bm, torch, synthdata, cfg, args.seed, i, lut, dev)[0] for i in range(NI)]
+    out = {}
+    for T, K in ((1, args.steps), (5, args.verify_steps)):
+        W = 10
+        n_x = K + W
+        xs = torch.from_numpy(synthdata.activations_bf16(args.seed, 30 + T, n_x * T, cfg.d_model).view(np.int16))
+        xs = xs.to(dev).view(torch.bfloat16).view(n_x, T, cfg.d_model)
+        ws = bm.workspace(layers[0], T, bm.MODE_DECODE_INT8)
+        ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, cfg.top_k), dtype=torch.float32, device=dev)
+        y = torch.empty((T, cfg.d_model), dtype=torch.bfloat16, device=dev)
+
+        def step(i):
+            L = layers[i % NI]
+            bm.route(L, xs[i], ws, ids=ids, weights=wts)
+            bm.expert_ffn(L, xs[i], ids, wts, ws, y=y, mode=bm.MODE_DECODE_INT8)
+
+        graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, not args.no_graph)
+        U = []
+        for i in range(W, W + K):
+            bm.route(layers[i % NI], xs[i], ws, ids=ids, weights=wts)
+            U.append(len(np.unique(ids.cpu().numpy())))
+        U_mean = float(np.mean(U))
+        P = T * cfg.top_k
+        alg = algorithmic_bytes(T, U_mean)
+        D, F = cfg.d_model, cfg.d_ff
+        # h travels as float32 (the quantiser's input)
+        alg["ffn_i8_gateup_kernel"] = U_mean * 2 * Q2_MAT + 2 * Q8_MAT + T * D * 2 + (P + T) * F * 4
+        alg["ffn_i8_down_kernel"] = U_mean * Q2_MAT + Q8_MAT + (P + T) * F * 4 + (P + T) * D * 4
+        step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
+        step_bytes = sum(alg[n] * prof[n][1] for n in prof if n in alg) / K
+        out[f"T{T}"] = {"tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 5),
+                        "union_mean": round(U_mean, 2), "hbm_gbps_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+                        "eager_ms_per_step": round(eager_ms / K, 5), "kernels": kernel_table(prof, alg)}
+        log(f"[bench] int8 decode T={T}: {step_ms * 1000:.2f} us/step")
+    out["workload"] = ("the decode layer (T=1) and a T=5 batch in int8 activation numerics: x and h quantised "
+                       "to 8-bit blocks of 32 values, integer dot products against the 2-bit and Q8_0 codes")
+    return out
+
+
 def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
     """Prefill chunk T=4096 through one layer with the Zipf router bias."""
     cfg = synthdata.CONFIGS["prefill"]
@@ -466,7 +512,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip every workload beside the decode line")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer stack workload")
-    ap.add_argument("--only", nargs="+", choices=["verify", "prefill", "router_variants", "engram_inject", "stack"],
+    ap.add_argument("--only", nargs="+",
+                    choices=["verify", "int8_decode", "prefill", "router_variants", "engram_inject", "stack"],
                     help="run only these of the workloads beside the decode line")
     ap.add_argument("--stack-prefill-steps", type=int, default=2)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -560,7 +607,7 @@ def main() -> int:
         "eager_ms_per_step": round(eager_ms / K, 5),
         "kernels": kernel_table(prof, alg),
     }
-    extras = (("verify", bench_verify), ("prefill", bench_prefill), ("router_variants", bench_router_variants),
+    extras = (("verify", bench_verify), ("int8_decode", bench_int8_decode), ("prefill", bench_prefill), ("router_variants", bench_router_variants),
               ("engram_inject", bench_engram_inject), ("stack", bench_stack))
     for name, fn in extras:
         if args.no_extra or (args.only and name not in args.only) or (name == "stack" and args.no_stack):

@@ -88,11 +88,16 @@ struct PrefillWs {
   float *y, *ys;
 };
 
-size_t carve_common(Carve &c, const bitmoe_layer *L, int T, int64_t **status, float **logits) {
+// Common region: status record, router logits and, for T > MAX_DECODE_T, the
+// router matrix's three bf16 parts (rewritten by every router call).
+size_t carve_common(Carve &c, const bitmoe_layer *L, int T, int64_t **status, float **logits,
+                    uint16_t **wsplit = nullptr) {
   void *st = c.take(256);
   void *lg = c.take(size_t(T) * L->n_experts * sizeof(float));
+  void *sp = c.take(T > MAX_DECODE_T ? bm::router_split_bytes(L->n_experts, L->d_model) : 0);
   if (status) *status = static_cast<int64_t *>(st);
   if (logits) *logits = static_cast<float *>(lg);
+  if (wsplit) *wsplit = T > MAX_DECODE_T ? static_cast<uint16_t *>(sp) : nullptr;
   return c.off;
 }
 
@@ -252,11 +257,12 @@ int moe_route(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, 
   Carve c(ws);
   int64_t *status;
   float *logits;
-  carve_common(c, L, T, &status, &logits);
+  uint16_t *wsplit;
+  carve_common(c, L, T, &status, &logits, &wsplit);
   if (ws_bytes < c.off)
     return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, c.off, T);
   hipError_t e = bm::launch_route(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k, L->w_router,
-                                  logit_bias, logits, topk_ids, topk_w, stream);
+                                  logit_bias, logits, topk_ids, topk_w, wsplit, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }
@@ -285,13 +291,14 @@ int moe_route_ex(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t 
   Carve c(ws);
   int64_t *status;
   float *logits;
-  carve_common(c, L, T, &status, &logits);
+  uint16_t *wsplit;
+  carve_common(c, L, T, &status, &logits, &wsplit);
   if (ws_bytes < c.off)
     return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, c.off, T);
   hipError_t e = bm::launch_route_variant(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k,
                                           L->w_router, opts->logit_bias, opts->score, opts->select_bias,
                                           opts->hash_table, opts->token_ids, opts->vocab, logits, topk_ids, topk_w,
-                                          status, stream);
+                                          status, wsplit, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }

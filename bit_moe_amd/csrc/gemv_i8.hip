@@ -52,6 +52,26 @@ constexpr int QBLK = 32;     // activation values per quantisation block
 constexpr int HALF = 16;     // values per stored sum
 constexpr int MAX_SLOTS = 8; // activation rows a block quantises at most (tokens or pairs of its job)
 
+// Tokens per pass for calls of T >= 2 (the pass's operands live in registers,
+// so it sets the kernel's register budget: at 4 tokens the kernels need ~200
+// VGPRs, two waves per SIMD) and row-iteration groups per chunk (routed;
+// shared: half) of the gate/up and down launches.  Measured at T = 5 (verify
+// batch, ~29 experts): gate/up 49 us with passes of 2 and 32-row chunks
+// against 68 us with passes of 4 and 16-row chunks; down 29.5 us with passes
+// of 1 (the shared job re-reads its chunk from L2) against 41 us.
+#ifndef BM_I8_NT_GU
+#define BM_I8_NT_GU 2
+#endif
+#ifndef BM_I8_NT_DN
+#define BM_I8_NT_DN 1
+#endif
+#ifndef BM_I8_GU_ITERS
+#define BM_I8_GU_ITERS 32
+#endif
+#ifndef BM_I8_DN_ITERS
+#define BM_I8_DN_ITERS 16
+#endif
+
 BM_DEVICE int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4(int(a), int(b), c, false); }
 
 // ---- quantiser --------------------------------------------------------------
@@ -450,18 +470,18 @@ __global__ void __launch_bounds__(256) q8_quantize_kernel(const void *x, int64_t
 
 }  // namespace
 
-// Routed gate/up chunks of 16 rows per wave-iteration group (4 rows per wave),
-// shared (Q8_0, 3.2x the bytes per row) 8; down: 32 and 16 rows.
+// Routed chunks of BM_I8_GU_ITERS (gate/up) and BM_I8_DN_ITERS (down) row
+// iterations, shared chunks (Q8_0, 3.2x the bytes per row) of half that.
 hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream) {
   a.u_max = a.T * a.k;
   const int rpi_gu = 64 / (a.D / 64), rpi_dn = 64 / (a.F / 64);
-  a.rows_gu = std::min(a.F, 16 * rpi_gu);
+  a.rows_gu = std::min(a.F, BM_I8_GU_ITERS * rpi_gu);
   a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
-  a.rows_sg = std::min(a.F, 8 * rpi_gu);
+  a.rows_sg = std::min(a.F, BM_I8_GU_ITERS / 2 * rpi_gu);
   a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
-  a.rows_dn = std::min(a.D, 16 * rpi_dn);
+  a.rows_dn = std::min(a.D, BM_I8_DN_ITERS * rpi_dn);
   a.chunks_dn = (a.D + a.rows_dn - 1) / a.rows_dn;
-  a.rows_sd = std::min(a.D, 8 * rpi_dn);
+  a.rows_sd = std::min(a.D, BM_I8_DN_ITERS / 2 * rpi_dn);
   a.chunks_sd = a.sd ? (a.D + a.rows_sd - 1) / a.rows_sd : 0;
   if (a.T > MAX_SLOTS) return hipErrorInvalidValue;
   const int slots = std::min(MAX_SLOTS, a.T * a.k);
@@ -475,10 +495,10 @@ hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
     BM_LAUNCH("ffn_i8_down_kernel", (ffn_i8_kernel<false, false, 1>), dim3(grid_dn), dim3(256), smem_dn, stream, a);
   } else {
-    if (xf32) BM_LAUNCH("ffn_i8_gateup_kernel", (ffn_i8_kernel<true, true, 4>), dim3(grid_gu), dim3(256), smem_gu, stream, a);
-    else BM_LAUNCH("ffn_i8_gateup_kernel", (ffn_i8_kernel<true, false, 4>), dim3(grid_gu), dim3(256), smem_gu, stream, a);
+    if (xf32) BM_LAUNCH("ffn_i8_gateup_kernel", (ffn_i8_kernel<true, true, BM_I8_NT_GU>), dim3(grid_gu), dim3(256), smem_gu, stream, a);
+    else BM_LAUNCH("ffn_i8_gateup_kernel", (ffn_i8_kernel<true, false, BM_I8_NT_GU>), dim3(grid_gu), dim3(256), smem_gu, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    BM_LAUNCH("ffn_i8_down_kernel", (ffn_i8_kernel<false, false, 4>), dim3(grid_dn), dim3(256), smem_dn, stream, a);
+    BM_LAUNCH("ffn_i8_down_kernel", (ffn_i8_kernel<false, false, BM_I8_NT_DN>), dim3(grid_dn), dim3(256), smem_dn, stream, a);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,

@@ -29,15 +29,18 @@ hipError_t launch_dequant(const void *blocks, int wfmt, int64_t n_weights, void 
 hipError_t launch_fill(void *dst, int64_t n_bytes, uint64_t key, int kind, const uint16_t *lut,
                        hipStream_t stream);
 hipError_t launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, int blocks, hipStream_t stream);
+// wsplit: router_split_bytes(E, D) of scratch for T > 8 (the router matrix's
+// exact bf16 parts), or null (then T > 8 runs the float32 tile kernel)
+size_t router_split_bytes(int E, int D);
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr, const float *bias,
-                        float *logits, int32_t *ids, float *wts, hipStream_t stream);
+                        float *logits, int32_t *ids, float *wts, uint16_t *wsplit, hipStream_t stream);
 
 // score: 0 softmax, 1 sqrt(softplus); select_bias and hash_table/token_ids
 // optional (see moe_route_ex)
 hipError_t launch_route_variant(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
                                 const float *logit_bias, int score, const float *select_bias,
                                 const int32_t *hash_table, const int32_t *token_ids, int64_t vocab, float *logits,
-                                int32_t *ids, float *wts, int64_t *status, hipStream_t stream);
+                                int32_t *ids, float *wts, int64_t *status, uint16_t *wsplit, hipStream_t stream);
 
 struct PlanBufs {
   int32_t *counts;

@@ -12,9 +12,9 @@
 //                order-independent)
 //  plan_scan     one block: per-expert prefix over chunks, exclusive scan over
 //                experts, union compaction, GEMM tile offsets
-//  plan_scatter  rank of each pair inside its chunk = number of earlier tokens
-//                of the chunk that chose the same expert (a token chooses an
-//                expert at most once), which keeps the order stable.
+//  plan_scatter  per chunk, the tokens in order: each pair takes the next
+//                slot of its expert (the chunk's base inside the expert's
+//                group, from plan_scan), which keeps the order stable.
 #include "common.h"
 #include "internal.h"
 
@@ -97,22 +97,25 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, in
 
 __global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restrict__ ids, int T, int k, int E,
                                                           PlanBufs p) {
-  extern __shared__ int32_t s_ids[];  // [64 * k]
+  extern __shared__ int32_t s_pos[];  // [E] next slot of each expert, then [64 * k] the chunk's ids
+  int32_t *s_ids = s_pos + E;
   const int chunk = blockIdx.x;
   const int t0 = chunk * 64;
   const int nt = min(64, T - t0);
+  for (int e = threadIdx.x; e < E; e += 64) s_pos[e] = p.offsets[e] + p.chunk_counts[int64_t(chunk) * E + e];
   for (int i = threadIdx.x; i < nt * k; i += 64) s_ids[i] = ids[int64_t(t0) * k + i];
   __syncthreads();
-  const int lt = threadIdx.x;
-  if (lt >= nt) return;
-  for (int j = 0; j < k; ++j) {
-    const int e = s_ids[lt * k + j];
+  // tokens of the chunk in order, lane j taking slot j: a token chooses an
+  // expert at most once, so the k lanes of a step advance distinct counters
+  // and each expert's pairs land in token order (stable)
+  const int j = threadIdx.x;
+  if (j >= k) return;
+  for (int u = 0; u < nt; ++u) {
+    const int e = s_ids[u * k + j];
     if (e < 0 || e >= E) continue;
-    int rank = 0;
-    for (int u = 0; u < lt; ++u)
-      for (int jj = 0; jj < k; ++jj) rank += (s_ids[u * k + jj] == e) ? 1 : 0;
-    const int pos = p.offsets[e] + p.chunk_counts[int64_t(chunk) * E + e] + rank;
-    p.perm[pos] = (t0 + lt) * k + j;
+    const int pos = s_pos[e];
+    s_pos[e] = pos + 1;
+    p.perm[pos] = (t0 + u) * k + j;
   }
 }
 
@@ -126,8 +129,8 @@ hipError_t launch_plan(const int32_t *ids, int T, int k, int E, int bm_tile, int
   BM_LAUNCH("plan_scan_kernel", plan_scan_kernel, dim3(1), dim3(1024), 0, stream, n_chunks, E, bm_tile, bm_tile2, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  BM_LAUNCH("plan_scatter_kernel", plan_scatter_kernel, dim3(n_chunks), dim3(64), 64 * k * sizeof(int32_t), stream, ids, T, k,
-                     E, p);
+  BM_LAUNCH("plan_scatter_kernel", plan_scatter_kernel, dim3(n_chunks), dim3(64), (E + 64 * k) * sizeof(int32_t), stream,
+            ids, T, k, E, p);
   return hipGetLastError();
 }
 

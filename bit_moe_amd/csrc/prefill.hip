@@ -442,6 +442,29 @@ static hipError_t launch_q8_expand(const void *blocks, int64_t n_weights, uint16
   return hipGetLastError();
 }
 
+// Routed grouped-GEMM tiles: 16 MI tokens (pairs) x 64 NG weight rows per
+// block (MI = 2 or 4: the plan's 32- and 64-row tile lists).  Measured on the
+// 4096-token chunk (gate/up, down): MI 2, NG 2 / MI 2, NG 4 take 2.71 / 1.98
+// ms; gate/up with 64-token tiles (MI 4, NG 1 or 2) 3.8-4.1 ms; down with
+// 64-pair tiles 6.3-10.5 ms (its double-buffered hi + lo rows then leave LDS
+// for one block per CU); gate/up NG 1 (4 waves per SIMD) 2.66 ms; down NG 2
+// or 1 3.0 / 4.7 ms.
+#ifndef BM_PF_GU_MI
+#define BM_PF_GU_MI 2
+#endif
+#ifndef BM_PF_GU_NG
+#define BM_PF_GU_NG 2
+#endif
+#ifndef BM_PF_DN_MI
+#define BM_PF_DN_MI 2
+#endif
+#ifndef BM_PF_DN_NG
+#define BM_PF_DN_NG 4
+#endif
+constexpr int GU_MI = BM_PF_GU_MI, GU_NG = BM_PF_GU_NG, DN_MI = BM_PF_DN_MI, DN_NG = BM_PF_DN_NG;
+static_assert((GU_MI == 2 || GU_MI == 4) && (DN_MI == 2 || DN_MI == 4), "M-tiles of 32 or 64 rows");
+static_assert(16 * 4 == PREFILL_BM && 16 * 2 == PREFILL_BM_DOWN, "tile lists of the plan");
+
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   if (a.D % KS || a.F % KS) return hipErrorNotSupported;  // K-steps of 256, N-tiles of 64
   hipError_t err;
@@ -466,9 +489,9 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.perm = p.perm;
   g.offsets = p.offsets;
   g.counts = p.counts;
-  // routed gate/up: A = x rows by token, N = F; tiles of 32 tokens x 128 rows
-  g.tile_off = p.tile_off2;
-  g.m_tiles = (P + PREFILL_BM_DOWN - 1) / PREFILL_BM_DOWN + min(a.E, P);
+  // routed gate/up: A = x rows by token, N = F; tiles of 16 GU_MI tokens x 64 GU_NG rows
+  g.tile_off = GU_MI == 4 ? p.tile_off : p.tile_off2;
+  g.m_tiles = (P + 16 * GU_MI - 1) / (16 * GU_MI) + min(a.E, P);
   g.a = x;
   g.a_by_pair = 0;
   g.K = a.D;
@@ -478,10 +501,10 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.b_expert_stride = q2_stride;
   g.h_out = a.h;
   g.h_lo_out = a.h_lo;
-  if ((err = launch_q2_gemm<true, 2, 2, false>(g, stream)) != hipSuccess) return err;
-  // routed down: A = h rows (hi + lo) by pair, N = D; tiles of 32 pairs x 256 rows
-  g.tile_off = p.tile_off2;
-  g.m_tiles = (P + PREFILL_BM_DOWN - 1) / PREFILL_BM_DOWN + min(a.E, P);
+  if ((err = launch_q2_gemm<true, GU_MI, GU_NG, false>(g, stream)) != hipSuccess) return err;
+  // routed down: A = h rows (hi + lo) by pair, N = D; tiles of 16 DN_MI pairs x 64 DN_NG rows
+  g.tile_off = DN_MI == 4 ? p.tile_off : p.tile_off2;
+  g.m_tiles = (P + 16 * DN_MI - 1) / (16 * DN_MI) + min(a.E, P);
   g.a = a.h;
   g.a_lo = a.h_lo;
   g.a_by_pair = 1;
@@ -490,7 +513,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.b0 = a.wd;
   g.b1 = nullptr;
   g.y_out = a.y;
-  if ((err = launch_q2_gemm<false, 2, 4, true>(g, stream)) != hipSuccess) return err;
+  if ((err = launch_q2_gemm<false, DN_MI, DN_NG, true>(g, stream)) != hipSuccess) return err;
 
   if (a.sg) {
     // shared expert: expand Q8_0 to exact bf16 codes + float scales, then dense GEMMs

@@ -11,14 +11,28 @@
 //                       its 16-byte slices of the row at once and keeps one
 //                       partial sum per token.  HBM-bound on the 4 B/weight
 //                       router matrix.
-//  router_tile_kernel   T > 8: 64 tokens x 64 experts per 256-thread block,
-//                       K staged through LDS in steps of 32, 4x4 outputs per
-//                       thread.
+//  router_split_kernel  T > 8, bf16 x: the float32 router matrix as three bf16
+//                       parts (stored in the MFMA operand order) hi = bf16(w), mid = bf16(w - hi), lo =
+//                       bf16(w - hi - mid).  Both differences are exact in
+//                       float32 and lo is exact in bf16 (w - hi - mid is a
+//                       multiple of w's float32 ulp below 2^8 of them), so
+//                       hi + mid + lo = w exactly.
+//  router_mfma_kernel   T > 8, bf16 x: logits = sum over the three parts of
+//                       x W_part^T on v_mfma_f32_16x16x32_bf16 (bf16 x bf16
+//                       products are exact in float32): 16 tokens x 64
+//                       experts per block, K split over its four waves, K
+//                       steps of 32 with the next step's operands loaded
+//                       ahead (each weight operand load is 1 KB of
+//                       contiguous bytes).
+//  router_tile_kernel   T > 8, float32 x: 64 tokens x 64 experts per
+//                       256-thread block, K staged through LDS in steps of
+//                       32, 4x4 outputs per thread.
 //  topk_kernel          one wave per token: k rounds of a wave-wide
 //                       maximum over order-preserving integer keys of the
 //                       logits (DPP), ties resolved by ballot.
 #include "common.h"
 #include "internal.h"
+#include "mfma_q2.h"
 
 namespace bm {
 
@@ -124,6 +138,142 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const void *__restrict
       if (e < E) logits[int64_t(t) * E + e] = acc[i][j] + (bias ? bias[e] : 0.f);
     }
   }
+}
+
+// Swizzled part layout: for part p, expert tile et (16 experts) and K step
+// ks (32 columns) one 1 KB record holding, for MFMA lane l, the 8 columns
+// 32 ks + 8 (l / 16) + 0..7 of expert 16 et + l % 16; records ordered
+// (p, et, ks).  A wave's operand load of one (p, et, ks) is then 1 KB of
+// contiguous bytes.
+BM_HOST_DEVICE inline size_t split_index(int p, int e, int k, int n_et, int D) {
+  const int et = e >> 4, ks = k >> 5, lane = (e & 15) + 16 * ((k & 31) >> 3);
+  return (((size_t(p) * n_et + et) * (D / 32) + ks) * 64 + lane) * 8 + (k & 7);
+}
+
+// Thread per 4 consecutive weights of a row (n = E * D, D a multiple of 256).
+__global__ void __launch_bounds__(256) router_split_kernel(const float *__restrict__ wr, int E, int D,
+                                                           uint16_t *__restrict__ parts) {
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= int64_t(E) * D) return;
+  const int e = int(i / D), k = int(i % D), n_et = (E + 15) / 16;
+  const float4 v = *reinterpret_cast<const float4 *>(wr + i);
+  const float w[4] = {v.x, v.y, v.z, v.w};
+  uint16_t h[4], m[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = f32_to_bf16(w[j]);
+    const float r1 = w[j] - bf16_to_f32(h[j]);
+    m[j] = f32_to_bf16(r1);
+    l[j] = f32_to_bf16(r1 - bf16_to_f32(m[j]));
+  }
+  const uint16_t *q[3] = {h, m, l};
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    *reinterpret_cast<uint2 *>(parts + split_index(p, e, k, n_et, D)) =
+        make_uint2(q[p][0] | (uint32_t(q[p][1]) << 16), q[p][2] | (uint32_t(q[p][3]) << 16));
+}
+
+// Lane layout of v_mfma_f32_16x16x32_bf16: A lane l holds row l % 16 and k =
+// 8 (l / 16) + 0..7, B lane l column l % 16 and the same k, the result lane l
+// rows 4 (l / 16) + 0..3 of column l % 16.  A block computes 16 tokens x 64
+// experts; its four waves take a quarter of K each (one step's loads in
+// flight ahead of its MFMAs: the K chain of a wave is what its latency
+// multiplies), and the partial sums are added in wave order through LDS.
+// Token rows past T read a clamped row, and neither they nor experts past E
+// are written.
+__global__ void __launch_bounds__(256) router_mfma_kernel(const uint16_t *__restrict__ x, int T, int D, int E,
+                                                          const uint16_t *__restrict__ parts,
+                                                          const float *__restrict__ bias,
+                                                          float *__restrict__ logits) {
+  __shared__ float red[4][4][4][64];  // [wave][expert tile][row r][lane]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 64;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int n_et = (E + 15) / 16, nks = D / 32, nq = nks / 4, ks0 = wave * nq;
+  const uint16_t *xa = x + size_t(min(t0 + r16, T - 1)) * D + kq;
+  // records of (part 0, expert tile e0/16 + n, step 0), this lane's 8 values
+  const uint16_t *wb = parts + (size_t(e0 >> 4) * nks * 64 + lane) * 8;
+  const size_t tile_stride = size_t(nks) * 512, part_stride = size_t(n_et) * tile_stride;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t A[4], B[4][3][4];
+  auto load = [&](int ks, uint32_t (&a)[4], uint32_t (&b)[4][3][4]) {
+    ld16(xa + 32 * ks, a);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) ld16(wb + p * part_stride + n * tile_stride + size_t(ks) * 512, b[n][p]);
+  };
+  load(ks0, A, B);
+  for (int ks = ks0; ks < ks0 + nq; ++ks) {
+    uint32_t An[4], Bn[4][3][4];
+    const bool more = ks + 1 < ks0 + nq;
+    if (more) load(ks + 1, An, Bn);
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) acc[n] = mfma16(A, B[n][p], acc[n]);
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) A[i] = An[i];
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int p = 0; p < 3; ++p)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) B[n][p][i] = Bn[n][p][i];
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][n][r][lane] = acc[n][r];
+  __syncthreads();
+  // wave w finishes expert tile w
+  const int e = e0 + 16 * wave + r16;
+  if (e >= E) return;
+  const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * (lane >> 4) + r;
+    const float v = ((red[0][wave][r][lane] + red[1][wave][r][lane]) + red[2][wave][r][lane]) + red[3][wave][r][lane];
+    if (t < T) logits[int64_t(t) * E + e] = v + b;
+  }
+}
+
+size_t router_split_bytes(int E, int D) { return size_t(3) * ((E + 63) / 64 * 64) * D * 2; }
+
+// Router logits for T tokens (wsplit: router_split_bytes(E, D) of scratch for
+// the swizzled bf16 parts, used for T > 8 with bf16 x).
+static hipError_t launch_logits(const void *x, bool xbf16, int T, int D, int E, const float *wr, const float *bias,
+                                float *logits, uint16_t *wsplit, hipStream_t stream) {
+  if (T <= 8) {
+    if (xbf16)
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr, bias,
+                logits);
+    else
+      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr, bias,
+                logits);
+  } else if (xbf16 && wsplit) {
+    const int64_t n = int64_t(E) * D;  // a multiple of 256 (D is)
+    BM_LAUNCH("router_split_kernel", router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, stream,
+              wr, E, D, wsplit);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid((T + 15) / 16, (E + 63) / 64);
+    BM_LAUNCH("router_mfma_kernel", router_mfma_kernel, grid, dim3(256), 0, stream,
+              static_cast<const uint16_t *>(x), T, D, E, wsplit, bias, logits);
+  } else {
+    const dim3 grid((T + 63) / 64, (E + 63) / 64);
+    if (xbf16)
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias,
+                logits);
+    else
+      BM_LAUNCH("router_tile_kernel", router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias,
+                logits);
+  }
+  return hipGetLastError();
 }
 
 // Order-preserving key of a float32 logit: larger value -> larger key, +0 and
@@ -322,24 +472,9 @@ __global__ void __launch_bounds__(256) topk_variant_kernel(const float *__restri
 hipError_t launch_route_variant(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
                                 const float *logit_bias, int score, const float *select_bias,
                                 const int32_t *hash_table, const int32_t *token_ids, int64_t vocab, float *logits,
-                                int32_t *ids, float *wts, int64_t *status, hipStream_t stream) {
-  if (T <= 8) {
-    if (xbf16)
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr,
-                logit_bias, logits);
-    else
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr,
-                logit_bias, logits);
-  } else {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    if (xbf16)
-      BM_LAUNCH("router_tile_kernel", router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr,
-                logit_bias, logits);
-    else
-      BM_LAUNCH("router_tile_kernel", router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr,
-                logit_bias, logits);
-  }
-  hipError_t err = hipGetLastError();
+                                int32_t *ids, float *wts, int64_t *status, uint16_t *wsplit,
+                                hipStream_t stream) {
+  hipError_t err = launch_logits(x, xbf16, T, D, E, wr, logit_bias, logits, wsplit, stream);
   if (err != hipSuccess) return err;
   const dim3 grid((T + 3) / 4), block(T == 1 ? 64 : 256);
   if (E <= 6 * 64)
@@ -352,21 +487,9 @@ hipError_t launch_route_variant(const void *x, bool xbf16, int T, int D, int E, 
 }
 
 hipError_t launch_route(const void *x, bool xbf16, int T, int D, int E, int k, const float *wr,
-                        const float *bias, float *logits, int32_t *ids, float *wts, hipStream_t stream) {
-  if (T <= 8) {
-    dim3 grid(E);
-    if (xbf16)
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
-    else
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
-  } else {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    if (xbf16)
-      BM_LAUNCH("router_tile_kernel", router_tile_kernel<true>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
-    else
-      BM_LAUNCH("router_tile_kernel", router_tile_kernel<false>, grid, dim3(256), 0, stream, x, T, D, E, wr, bias, logits);
-  }
-  hipError_t err = hipGetLastError();
+                        const float *bias, float *logits, int32_t *ids, float *wts, uint16_t *wsplit,
+                        hipStream_t stream) {
+  hipError_t err = launch_logits(x, xbf16, T, D, E, wr, bias, logits, wsplit, stream);
   if (err != hipSuccess) return err;
   // blocks of 4 waves for T > 1; a single wave for one token
   const dim3 grid((T + 3) / 4), block(T == 1 ? 64 : 256);

@@ -109,7 +109,7 @@ def test_int8_full_decode_layer(T):
 @pytest.mark.parametrize("T", [5, 8])
 def test_int8_tokens_sharing_experts(T):
     # every token picks the same five experts (rotated) and one of its own:
-    # routed jobs of T pairs run in passes of four and two tokens
+    # routed jobs of T pairs run in token passes (of two in gate/up, one in down)
     ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 8)
     common = np.array([3, 77, 150, 211, 300, 383])
     ids_h = np.stack([np.roll(common, t) for t in range(T)])
