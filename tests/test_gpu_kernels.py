@@ -152,6 +152,17 @@ def test_router_decode_shapes(T):
     assert exact + ties == T
 
 
+@pytest.mark.parametrize("T,d,E,k,xd", [(9, 256, 16, 2, "bf16"), (33, 1024, 100, 6, "bf16"), (130, 512, 1000, 8, "bf16"),
+                                        (70, 4096, 64, 1, "bf16"), (40, 256, 100, 4, "f32")])
+def test_router_ragged_shapes(T, d, E, k, xd):
+    # T > 8 with bf16 x runs the logits on MFMA over the router matrix's three
+    # bf16 parts (token tiles of 16, expert tiles of 64, ragged ends on both
+    # sides); float32 x keeps the float32 tile kernel
+    cfg = synthdata.Config(f"router-{T}-{d}-{E}", T, d, 256, E, k, xd, False)
+    exact, ties = _route_check(synthdata.LayerData(cfg, 9), tag=T)
+    assert exact + ties == T
+
+
 def test_router_prefill_zipf_bias():
     ld = synthdata.LayerData(synthdata.CONFIGS["prefill"], 1)
     exact, ties = _route_check(ld, bias=ld.bias())
