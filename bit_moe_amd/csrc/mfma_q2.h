@@ -3,9 +3,10 @@
 // A weight of sub-block s is w_k = d*sc_s*q_k - dmin*m_s, so a row's dot
 // product with activations x over one 256-weight super-block is
 //   d * sum_k (sc_s q_k) x_k  -  dmin * sum_s m_s X_s,   X_s = sum_{k in s} x_k.
-// sc*q (0..45) and m (0..15) are small integers, exact in bf16: eight MFMAs
-// on B = sc*q and one MFMA on B = m (against X_s split into bf16 hi + lo) give
-// the two sums in float32, and d, dmin scale them afterwards.
+// sc*q (0..45) and m (0..15) are small integers, and 128 + sc*q is exact in
+// bf16 too: eight MFMAs on B = 128 + sc*q, one MFMA on B = m and one on B =
+// 128 (both against X_s split into bf16 hi + lo) give the sums in float32 (the
+// last one removes the offset), and d, dmin scale them afterwards.
 //
 // Lane k-slots (MFMA 16x16x32: A lane l holds row l%16 and k = 8*(l/16)+0..7,
 // B lane l holds column l%16 and the same k, D lane l holds rows 4*(l/16)+0..3
@@ -31,27 +32,6 @@ typedef q2u32x2 __attribute__((aligned(4))) q2u32x2_a4;
 // bf16 bits of a small non-negative integer (exact)
 BM_DEVICE uint32_t bf16_of_small(uint32_t v) { return __float_as_uint(float(v)) >> 16; }
 
-// four codes (bytes 0..3, each 0..3) -> two bf16 pairs via a 4-entry table
-// given as its low bytes (tlo) and high bytes (thi)
-BM_DEVICE void lookup4(uint32_t codes, uint32_t tlo, uint32_t thi, uint32_t &p01, uint32_t &p23) {
-  const uint32_t lo = __builtin_amdgcn_perm(0u, tlo, codes);
-  const uint32_t hi = __builtin_amdgcn_perm(0u, thi, codes);
-  p01 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-  p23 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
-}
-
-// Table of bf16(sc*q), q = 0..3, for every scale sc: tab[sc] = (low bytes, high bytes).
-BM_DEVICE uint2 sc_table_entry(uint32_t sc) {
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int q = 1; q < 4; ++q) {
-    const uint32_t v = bf16_of_small(sc * q);
-    lo |= (v & 0xFFu) << (8 * q);
-    hi |= (v >> 8) << (8 * q);
-  }
-  return make_uint2(lo, hi);
-}
-
 // Raw bytes of one lane's quarter of a super-block.
 struct Q2Raw {
   q2u32x4 q;    // 16 code bytes at 16 + 32h + 16p
@@ -74,14 +54,23 @@ BM_DEVICE Q2Raw q2_load(const uint8_t *sb, int g) {
   return r;
 }
 
-// Main operands for MFMA step t (8 weights) from the raw bytes.
-BM_DEVICE void q2_main_operand(const Q2Raw &r, int p, int t, const uint2 *tab, uint32_t (&B)[4]) {
+// Main operands for MFMA step t (8 weights) from the raw bytes, in offset
+// form: bf16 bits 0x43vv are the value 128 + vv for vv < 128, so the bytes v
+// = sc*q (0..45) of a per-scale byte table (one multiply) become bf16
+// operands 128 + sc*q with one byte interleave per pair: two table perms and
+// four interleave perms per 8 weights.  The MFMA then sums (128 + sc q) x;
+// the caller removes 128 * (sum of x over the super-block).
+BM_DEVICE void q2_main_operand(const Q2Raw &r, int p, int t, uint32_t (&B)[4]) {
   const int s = t >> 1, j8 = t & 1;
   const uint32_t scw = (s < 2 ? r.sc.x : r.sc.y) >> (8 * p + 16 * (s & 1));
-  const uint2 tb = tab[scw & 0xFu];
+  const uint32_t tab = (scw & 0xFu) * 0x03020100u;  // bytes 0, sc, 2 sc, 3 sc (3 * 15 < 256: no carries)
   const uint32_t w0 = j8 ? r.q.z : r.q.x, w1 = j8 ? r.q.w : r.q.y;
-  lookup4((w0 >> (2 * s)) & 0x03030303u, tb.x, tb.y, B[0], B[1]);
-  lookup4((w1 >> (2 * s)) & 0x03030303u, tb.x, tb.y, B[2], B[3]);
+  const uint32_t v0 = __builtin_amdgcn_perm(0u, tab, (w0 >> (2 * s)) & 0x03030303u);
+  const uint32_t v1 = __builtin_amdgcn_perm(0u, tab, (w1 >> (2 * s)) & 0x03030303u);
+  B[0] = __builtin_amdgcn_perm(0x43434343u, v0, 0x04010400u);  // (v0.b0, v0.b1) as 0x43vv words
+  B[1] = __builtin_amdgcn_perm(0x43434343u, v0, 0x04030402u);
+  B[2] = __builtin_amdgcn_perm(0x43434343u, v1, 0x04010400u);
+  B[3] = __builtin_amdgcn_perm(0x43434343u, v1, 0x04030402u);
 }
 
 // Min operand: slot i = 2s + part holds m of sub-block 8h + 2s + p.

@@ -200,8 +200,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   constexpr int BUF = PARTS * BMt * ROWB;  // bytes per buffer half
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_q2[];
   uint16_t *Xs = reinterpret_cast<uint16_t *>(smem_q2 + 2 * BUF);  // [BMt][XS_ROW]
-  uint2 *tab = reinterpret_cast<uint2 *>(Xs + BMt * XS_ROW);       // [16]
-  int32_t *rows = reinterpret_cast<int32_t *>(tab + 16);           // [BMt] activation row, -1: none
+  int32_t *rows = reinterpret_cast<int32_t *>(Xs + BMt * XS_ROW);  // [BMt] activation row, -1: none
   const int nt_n = a.N / BNt;
   // XCD-aware remap of the block index (grid is a multiple of 8)
   const int G = gridDim.x, b = blockIdx.x;
@@ -219,7 +218,6 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   const int base = a.offsets[e] + m0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, nl = lane & 15, p = g & 1;
-  if (tid < 16) tab[tid] = sc_table_entry(tid);
   for (int i = tid; i < BMt; i += 256) {
     int r = -1;
     if (i < valid) {
@@ -307,7 +305,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) q2_main_operand(cur[ng][m], p, t, tab, B[ng][m]);
+        for (int m = 0; m < NM; ++m) q2_main_operand(cur[ng][m], p, t, B[ng][m]);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         uint32_t A[4];
@@ -324,6 +322,18 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
       }
     }
     // min term against the sums, then d and dmin of the super-block
+    uint32_t As[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As[mi]);
+    // 128 * (sum of the row's activations over the super-block), the offset
+    // of the main operands: the sums (hi + lo parts of all 16 sub-blocks)
+    // against a constant 128 operand
+    f32x4_t cx[MI];
+    {
+      const uint32_t B128[4] = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) cx[mi] = mfma16(As[mi], B128, zero);
+    }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
 #pragma unroll
@@ -333,12 +343,12 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
         const float d = q2_d(cur[ng][m]), dm = q2_dmin(cur[ng][m]);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          uint32_t As[4];
-          ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As);
-          const f32x4_t cn = mfma16(As, Bn, zero);
+          const f32x4_t cn = mfma16(As[mi], Bn, zero);
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[mi][ng][m][r] = __builtin_fmaf(d, cm[mi][ng][m][r], __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
+          for (int r = 0; r < 4; ++r) {
+            const float main = cm[mi][ng][m][r] - cx[mi][r];
+            acc[mi][ng][m][r] = __builtin_fmaf(d, main, __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
+          }
         }
       }
     }
@@ -378,7 +388,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
 
 template <bool GATEUP, int MI, int NG, bool ALO>
 static size_t q2_gemm_smem() {
-  return size_t(2) * (ALO ? 2 : 1) * 16 * MI * LDS_ROW * 2 + size_t(16) * MI * XS_ROW * 2 + 16 * 8 + size_t(16) * MI * 4;
+  return size_t(2) * (ALO ? 2 : 1) * 16 * MI * LDS_ROW * 2 + size_t(16) * MI * XS_ROW * 2 + size_t(16) * MI * 4;
 }
 
 template <bool GATEUP, int MI, int NG, bool ALO>
