@@ -163,3 +163,17 @@ def test_int8_deterministic():
     y1 = bm.expert_ffn(layer, x, ids, w, ws, mode=bm.MODE_DECODE_INT8).clone()
     y2 = bm.expert_ffn(layer, x, ids, w, ws, mode=bm.MODE_DECODE_INT8)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [bm.MODE_AUTO, bm.MODE_DECODE, bm.MODE_PREFILL, bm.MODE_DECODE_INT8])
+def test_empty_batch_every_mode(mode):
+    # T = 0: the router and the expert call launch nothing and return empty outputs
+    ld = synthdata.LayerData(SMALL, 25)
+    layer = device_layer(ld, host_bytes=True)
+    x = torch.zeros((0, SMALL.d_model), dtype=torch.bfloat16, device="cuda")
+    ws = bm.workspace(layer, 0, mode)
+    ids, w = bm.route(layer, x, ws)
+    y = bm.expert_ffn(layer, x, ids, w, ws, mode=mode)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, SMALL.top_k) and w.shape == (0, SMALL.top_k) and y.shape == (0, SMALL.d_model)
+    assert bm.read_status(bm.ws_status(ws))[0] == 0
