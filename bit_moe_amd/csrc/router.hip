@@ -34,6 +34,8 @@
 #include "internal.h"
 #include "mfma_q2.h"
 
+#include <type_traits>
+
 namespace bm {
 
 template <bool XBF16>
@@ -47,14 +49,16 @@ BM_DEVICE float4 load_x4(const void *x, int64_t idx) {
 }
 
 // One block per expert row: thread i reads the float4 slices 4i + 1024j of the
-// row (all of them issued before the arithmetic), the block sums through LDS.
-template <bool XBF16>
+// row and its slices of every token's activations (all of them issued before
+// the arithmetic; NT >= T token slots, those past T re-read token T-1 and are
+// dropped), the block sums through LDS.
+template <bool XBF16, int NT>
 __global__ void __launch_bounds__(256) router_gemv_kernel(const void *__restrict__ x, int T, int D, int E,
                                                           const float *__restrict__ wr,
                                                           const float *__restrict__ bias,
                                                           float *__restrict__ logits) {
   constexpr int MAXJ = 4;  // D <= 4096
-  __shared__ float part[4][8];
+  __shared__ float part[4][NT];
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float *row = wr + int64_t(e) * D;
@@ -64,24 +68,37 @@ __global__ void __launch_bounds__(256) router_gemv_kernel(const void *__restrict
     const int c = 4 * tid + 1024 * j;
     w[j] = c < D ? *reinterpret_cast<const float4 *>(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  // raw activation slices: 4 bf16 (uint2) or 4 float32 (float4) per slot
+  typename std::conditional<XBF16, uint2, float4>::type xv[NT][MAXJ];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    if (t < T) {
-      float acc = 0.f;
+  for (int t = 0; t < NT; ++t) {
+    const int64_t tt = min(t, T - 1);
 #pragma unroll
-      for (int j = 0; j < MAXJ; ++j) {
-        const int c = 4 * tid + 1024 * j;
-        if (c < D) {
-          const float4 v = load_x4<XBF16>(x, int64_t(t) * D + c);
-          acc = __builtin_fmaf(w[j].x, v.x, acc);
-          acc = __builtin_fmaf(w[j].y, v.y, acc);
-          acc = __builtin_fmaf(w[j].z, v.z, acc);
-          acc = __builtin_fmaf(w[j].w, v.w, acc);
-        }
-      }
-      const float s = wave_sum(acc);
-      if (lane == 0) part[wave][t] = s;
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = 4 * tid + 1024 * j;
+      if constexpr (XBF16)
+        xv[t][j] = c < D ? *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + tt * D + c)
+                         : make_uint2(0u, 0u);
+      else
+        xv[t][j] = c < D ? *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + tt * D + c)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      float4 v;
+      if constexpr (XBF16) v = make_float4(bf16_lo(xv[t][j].x), bf16_hi(xv[t][j].x), bf16_lo(xv[t][j].y), bf16_hi(xv[t][j].y));
+      else v = xv[t][j];
+      acc = __builtin_fmaf(w[j].x, v.x, acc);
+      acc = __builtin_fmaf(w[j].y, v.y, acc);
+      acc = __builtin_fmaf(w[j].z, v.z, acc);
+      acc = __builtin_fmaf(w[j].w, v.w, acc);
+    }
+    const float s = wave_sum(acc);
+    if (lane == 0) part[wave][t] = s;
   }
   __syncthreads();
   if (tid < T) {
@@ -249,12 +266,22 @@ size_t router_split_bytes(int E, int D) { return size_t(3) * ((E + 63) / 64 * 64
 static hipError_t launch_logits(const void *x, bool xbf16, int T, int D, int E, const float *wr, const float *bias,
                                 float *logits, uint16_t *wsplit, hipStream_t stream) {
   if (T <= 8) {
-    if (xbf16)
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<true>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr, bias,
-                logits);
-    else
-      BM_LAUNCH("router_gemv_kernel", router_gemv_kernel<false>, dim3(E), dim3(256), 0, stream, x, T, D, E, wr, bias,
-                logits);
+    // token slots per block: the smallest of 1, 2, 4, 8 that holds T
+#define BM_ROUTER_GEMV(XB, NT)                                                                                   \
+  BM_LAUNCH("router_gemv_kernel", (router_gemv_kernel<XB, NT>), dim3(E), dim3(256), 0, stream, x, T, D, E, wr, bias, \
+            logits)
+    if (xbf16) {
+      if (T == 1) BM_ROUTER_GEMV(true, 1);
+      else if (T == 2) BM_ROUTER_GEMV(true, 2);
+      else if (T <= 4) BM_ROUTER_GEMV(true, 4);
+      else BM_ROUTER_GEMV(true, 8);
+    } else {
+      if (T == 1) BM_ROUTER_GEMV(false, 1);
+      else if (T == 2) BM_ROUTER_GEMV(false, 2);
+      else if (T <= 4) BM_ROUTER_GEMV(false, 4);
+      else BM_ROUTER_GEMV(false, 8);
+    }
+#undef BM_ROUTER_GEMV
   } else if (xbf16 && wsplit) {
     const int64_t n = int64_t(E) * D;  // a multiple of 256 (D is)
     BM_LAUNCH("router_split_kernel", router_split_kernel, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, stream,
