@@ -289,13 +289,24 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
       Xs[r * XS_ROW + q2_sum_slot(sb, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
     }
     __syncthreads();
+    // the step's sub-block sums (hi + lo, min-slot order) and -128 times the
+    // sum of each row's activations over the super-block: the main
+    // accumulators start from it, which removes the 128 offset of the main
+    // operands without a subtraction per output
+    uint32_t As[MI][4];
     f32x4_t cm[MI][NG][NM];
+    {
+      const uint32_t Bm128[4] = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MI; ++mi) {
+        ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As[mi]);
+        const f32x4_t cx = mfma16(As[mi], Bm128, zero);
 #pragma unroll
-      for (int ng = 0; ng < NG; ++ng)
+        for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) cm[mi][ng][m] = zero;
+          for (int m = 0; m < NM; ++m) cm[mi][ng][m] = cx;
+      }
+    }
     const uint16_t *Ah = reinterpret_cast<const uint16_t *>(cb);
     const uint16_t *Al = reinterpret_cast<const uint16_t *>(cb + BMt * ROWB);
 #pragma unroll
@@ -322,18 +333,6 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
       }
     }
     // min term against the sums, then d and dmin of the super-block
-    uint32_t As[MI][4];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As[mi]);
-    // 128 * (sum of the row's activations over the super-block), the offset
-    // of the main operands: the sums (hi + lo parts of all 16 sub-blocks)
-    // against a constant 128 operand
-    f32x4_t cx[MI];
-    {
-      const uint32_t B128[4] = {0x43004300u, 0x43004300u, 0x43004300u, 0x43004300u};
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) cx[mi] = mfma16(As[mi], B128, zero);
-    }
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
 #pragma unroll
@@ -345,10 +344,8 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
         for (int mi = 0; mi < MI; ++mi) {
           const f32x4_t cn = mfma16(As[mi], Bn, zero);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float main = cm[mi][ng][m][r] - cx[mi][r];
-            acc[mi][ng][m][r] = __builtin_fmaf(d, main, __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
-          }
+          for (int r = 0; r < 4; ++r)
+            acc[mi][ng][m][r] = __builtin_fmaf(d, cm[mi][ng][m][r], __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
         }
       }
     }
