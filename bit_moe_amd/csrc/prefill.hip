@@ -192,7 +192,8 @@ __global__ void __launch_bounds__(256) q8x_gemm_kernel(GemmArgs a) {
 // weight bytes of kb+1 are loaded into registers; the block waits for both
 // once per step.  The sub-block sums of the step's rows are formed from LDS.
 // Per wave and step: 8 x MI x NG x NM main MFMAs (+ the lo parts) on exact
-// B = bf16(sc*q), and MI x NG x NM min MFMAs against the sums.
+// B = bf16(128 + sc*q), MI MFMAs for the offset and MI x NG x NM min MFMAs
+// against the sums.
 template <bool GATEUP, int MI, int NG, bool ALO>
 __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   constexpr int BMt = 16 * MI, BNt = 64 * NG, PARTS = ALO ? 2 : 1, NM = GATEUP ? 2 : 1;
@@ -282,7 +283,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
         const uint4 v0 = v[0], v1 = v[1];
         const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) sum += bf16_lo(w8[i]) + bf16_hi(w8[i]);
+        for (int i = 0; i < 8; ++i) sum = dot2_bf16(w8[i], 0x3F803F80u, sum);  // + lo + hi (bf16 1.0 pair)
       }
       const uint16_t shi = f32_to_bf16(sum);
       Xs[r * XS_ROW + q2_sum_slot(sb, 0)] = shi;
