@@ -194,6 +194,98 @@ __global__ void __launch_bounds__(256) q8x_gemm_kernel(GemmArgs a) {
 // Per wave and step: 8 x MI x NG x NM main MFMAs (+ the lo parts) on exact
 // B = bf16(128 + sc*q), MI MFMAs for the offset and MI x NG x NM min MFMAs
 // against the sums.
+// One K-step of the routed grouped GEMM for a block's wave: the sub-block
+// sums of the step's BMt activation rows (all parts, from the LDS half cb) into
+// Xs as bf16 hi + lo, then per wave: -128 x the rows' super-block sums as the
+// start of the main accumulators, eight MFMA steps on the offset operands of
+// the weight bytes cur, the min term against the sums, and d, dmin into acc.
+// Contains one block barrier (the sums are shared by the block's waves).
+template <int MI, int NG, int NM, bool ALO>
+BM_DEVICE void q2_step(const uint8_t *cb, uint16_t *Xs, const Q2Raw (&cur)[NG][NM], f32x4_t (&acc)[MI][NG][NM]) {
+  constexpr int BMt = 16 * MI, PARTS = ALO ? 2 : 1;
+  constexpr int ROWB = LDS_ROW * 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = lane >> 4, nl = lane & 15, p = g & 1;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  // sub-block sums of the step's rows (all parts), split into bf16 hi + lo
+  for (int idx = tid; idx < BMt * 16; idx += 256) {
+    const int r = idx >> 4, sb = idx & 15;
+    float sum = 0.f;
+#pragma unroll
+    for (int part = 0; part < PARTS; ++part) {
+      const uint4 *v = reinterpret_cast<const uint4 *>(cb + (part * BMt + r) * ROWB + sb * 32);
+      const uint4 v0 = v[0], v1 = v[1];
+      const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum = dot2_bf16(w8[i], 0x3F803F80u, sum);  // + lo + hi (bf16 1.0 pair)
+    }
+    const uint16_t shi = f32_to_bf16(sum);
+    Xs[r * XS_ROW + q2_sum_slot(sb, 0)] = shi;
+    Xs[r * XS_ROW + q2_sum_slot(sb, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
+  }
+  __syncthreads();
+  // the step's sub-block sums (hi + lo, min-slot order) and -128 times the
+  // sum of each row's activations over the super-block: the main
+  // accumulators start from it, which removes the 128 offset of the main
+  // operands without a subtraction per output
+  uint32_t As[MI][4];
+  f32x4_t cm[MI][NG][NM];
+  {
+    const uint32_t Bm128[4] = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As[mi]);
+      const f32x4_t cx = mfma16(As[mi], Bm128, zero);
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) cm[mi][ng][m] = cx;
+    }
+  }
+  const uint16_t *Ah = reinterpret_cast<const uint16_t *>(cb);
+  const uint16_t *Al = reinterpret_cast<const uint16_t *>(cb + BMt * ROWB);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int ko = q2_kofs(t, g);
+    uint32_t B[NG][NM][4];
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) q2_main_operand(cur[ng][m], p, t, B[ng][m]);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      uint32_t A[4];
+      ld16(Ah + (16 * mi + nl) * LDS_ROW + ko, A);
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) cm[mi][ng][m] = mfma16(A, B[ng][m], cm[mi][ng][m]);
+      if constexpr (ALO) {
+        ld16(Al + (16 * mi + nl) * LDS_ROW + ko, A);
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) cm[mi][ng][0] = mfma16(A, B[ng][0], cm[mi][ng][0]);
+      }
+    }
+  }
+  // min term against the sums, then d and dmin of the super-block
+#pragma unroll
+  for (int ng = 0; ng < NG; ++ng) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      uint32_t Bn[4];
+      q2_min_operand(cur[ng][m], p, Bn);
+      const float d = q2_d(cur[ng][m]), dm = q2_dmin(cur[ng][m]);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const f32x4_t cn = mfma16(As[mi], Bn, zero);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[mi][ng][m][r] = __builtin_fmaf(d, cm[mi][ng][m][r], __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
+      }
+    }
+  }
+}
+
 template <bool GATEUP, int MI, int NG, bool ALO>
 __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   constexpr int BMt = 16 * MI, BNt = 64 * NG, PARTS = ALO ? 2 : 1, NM = GATEUP ? 2 : 1;
@@ -218,7 +310,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   const int valid = min(BMt, a.counts[e] - m0);
   const int base = a.offsets[e] + m0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, nl = lane & 15, p = g & 1;
+  const int g = lane >> 4, nl = lane & 15;
   for (int i = tid; i < BMt; i += 256) {
     int r = -1;
     if (i < valid) {
@@ -272,84 +364,7 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
       issue_a(kb + 1, (kb + 1) & 1);
       load_b(kb + 1, nxt);
     }
-    const uint8_t *cb = smem_q2 + (kb & 1) * BUF;
-    // sub-block sums of the step's rows (all parts), split into bf16 hi + lo
-    for (int idx = tid; idx < BMt * 16; idx += 256) {
-      const int r = idx >> 4, sb = idx & 15;
-      float sum = 0.f;
-#pragma unroll
-      for (int part = 0; part < PARTS; ++part) {
-        const uint4 *v = reinterpret_cast<const uint4 *>(cb + (part * BMt + r) * ROWB + sb * 32);
-        const uint4 v0 = v[0], v1 = v[1];
-        const uint32_t w8[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) sum = dot2_bf16(w8[i], 0x3F803F80u, sum);  // + lo + hi (bf16 1.0 pair)
-      }
-      const uint16_t shi = f32_to_bf16(sum);
-      Xs[r * XS_ROW + q2_sum_slot(sb, 0)] = shi;
-      Xs[r * XS_ROW + q2_sum_slot(sb, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
-    }
-    __syncthreads();
-    // the step's sub-block sums (hi + lo, min-slot order) and -128 times the
-    // sum of each row's activations over the super-block: the main
-    // accumulators start from it, which removes the 128 offset of the main
-    // operands without a subtraction per output
-    uint32_t As[MI][4];
-    f32x4_t cm[MI][NG][NM];
-    {
-      const uint32_t Bm128[4] = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        ld16(Xs + (16 * mi + nl) * XS_ROW + 8 * g, As[mi]);
-        const f32x4_t cx = mfma16(As[mi], Bm128, zero);
-#pragma unroll
-        for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) cm[mi][ng][m] = cx;
-      }
-    }
-    const uint16_t *Ah = reinterpret_cast<const uint16_t *>(cb);
-    const uint16_t *Al = reinterpret_cast<const uint16_t *>(cb + BMt * ROWB);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int ko = q2_kofs(t, g);
-      uint32_t B[NG][NM][4];
-#pragma unroll
-      for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) q2_main_operand(cur[ng][m], p, t, B[ng][m]);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        uint32_t A[4];
-        ld16(Ah + (16 * mi + nl) * LDS_ROW + ko, A);
-#pragma unroll
-        for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) cm[mi][ng][m] = mfma16(A, B[ng][m], cm[mi][ng][m]);
-        if constexpr (ALO) {
-          ld16(Al + (16 * mi + nl) * LDS_ROW + ko, A);
-#pragma unroll
-          for (int ng = 0; ng < NG; ++ng) cm[mi][ng][0] = mfma16(A, B[ng][0], cm[mi][ng][0]);
-        }
-      }
-    }
-    // min term against the sums, then d and dmin of the super-block
-#pragma unroll
-    for (int ng = 0; ng < NG; ++ng) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        uint32_t Bn[4];
-        q2_min_operand(cur[ng][m], p, Bn);
-        const float d = q2_d(cur[ng][m]), dm = q2_dmin(cur[ng][m]);
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-          const f32x4_t cn = mfma16(As[mi], Bn, zero);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[mi][ng][m][r] = __builtin_fmaf(d, cm[mi][ng][m][r], __builtin_fmaf(-dm, cn[r], acc[mi][ng][m][r]));
-        }
-      }
-    }
+    q2_step<MI, NG, NM, ALO>(smem_q2 + (kb & 1) * BUF, Xs, cur, acc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows and weight bytes have landed
     __syncthreads();  // ... and this step's buffer half and sums are no longer read
 #pragma unroll
@@ -384,6 +399,129 @@ __global__ void __launch_bounds__(256, 2) q2_gemm_kernel(GemmArgs a) {
   }
 }
 
+// Routed gate/up grouped GEMM with the weight bytes two steps ahead.  Same
+// tiles, operands and arithmetic as q2_gemm_kernel<true, ...>; the activation
+// rows of step kb+1 are loaded into registers at the start of step kb and
+// written to the other LDS half at its end, and the weight bytes of step kb+2
+// are loaded into the third of three register sets.  Every load is a plain
+// one, so the compiler's waits count them exactly: computing step kb waits
+// only for its own weight bytes (requested two steps earlier), writing the
+// activations of kb+1 only for those.  The K loop is unrolled by three so the
+// register sets rotate without copies.
+template <int MI, int NG>
+__global__ void __launch_bounds__(256, 2) q2_gemm_p3_kernel(GemmArgs a) {
+  constexpr int BMt = 16 * MI, BNt = 64 * NG, NM = 2;
+  constexpr int ROWB = LDS_ROW * 2;              // bytes per LDS activation row
+  constexpr int BUF = BMt * ROWB;                // bytes per buffer half
+  constexpr int APT = BMt * KS * 2 / 256 / 16;   // 16-byte activation slices per thread and step
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem_q2[];
+  uint16_t *Xs = reinterpret_cast<uint16_t *>(smem_q2 + 2 * BUF);  // [BMt][XS_ROW]
+  int32_t *rows = reinterpret_cast<int32_t *>(Xs + BMt * XS_ROW);  // [BMt] activation row, -1: none
+  const int nt_n = a.N / BNt;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int L = (b & 7) * (G >> 3) + (b >> 3);  // XCD-aware remap (grid is a multiple of 8)
+  const int mt = L / nt_n, ntile = L % nt_n;
+  if (mt >= a.m_tiles || mt >= a.tile_off[a.E]) return;
+  int lo = 0, hi = a.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.tile_off[mid] <= mt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int m0 = (mt - a.tile_off[e]) * BMt;
+  const int valid = min(BMt, a.counts[e] - m0);
+  const int base = a.offsets[e] + m0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, nl = lane & 15;
+  for (int i = tid; i < BMt; i += 256) {
+    int r = -1;
+    if (i < valid) r = a.perm[base + i] / a.k;
+    rows[i] = r;
+  }
+  __syncthreads();
+  const size_t row_bytes = size_t(a.K) / 256 * 84;
+  const uint8_t *wb[2] = {a.b0 + size_t(e) * a.b_expert_stride, a.b1 + size_t(e) * a.b_expert_stride};
+  const int n_w = ntile * BNt + wave * 16 * NG + nl;
+  // this thread's activation slices: 16 bytes each; slice sl is 16-byte piece
+  // sl % 32 of row sl / 32 (a step's row is 512 bytes)
+  const uint16_t *asrc[APT];
+  int adst[APT];
+#pragma unroll
+  for (int j = 0; j < APT; ++j) {
+    const int sl = tid * APT + j, r = sl >> 5, c = sl & 31;
+    const int src_row = rows[r];
+    asrc[j] = src_row >= 0 ? a.a + size_t(src_row) * a.K + 8 * c : nullptr;
+    adst[j] = r * ROWB + 16 * c;
+  }
+  auto load_a = [&](int kb, uint4 (&av)[APT]) {
+#pragma unroll
+    for (int j = 0; j < APT; ++j)
+      av[j] = asrc[j] ? *reinterpret_cast<const uint4 *>(asrc[j] + kb * KS) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto store_a = [&](int half, const uint4 (&av)[APT]) {
+#pragma unroll
+    for (int j = 0; j < APT; ++j) *reinterpret_cast<uint4 *>(smem_q2 + half * BUF + adst[j]) = av[j];
+  };
+  auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) raw[ng][m] = q2_load(wb[m] + size_t(n_w + 16 * ng) * row_bytes + size_t(kb) * 84, g);
+  };
+  f32x4_t acc[MI][NG][NM];
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[mi][ng][m] = zero;
+  const int nsteps = a.K / KS;
+  // one K-step: compute with cur (weights of kb), request the weights of kb+2
+  // into fill and the activations of kb+1, write those to the other LDS half
+  auto step = [&](int kb, const Q2Raw (&cur)[NG][NM], Q2Raw (&fill)[NG][NM]) {
+    uint4 av[APT];
+    if (kb + 1 < nsteps) load_a(kb + 1, av);
+    if (kb + 2 < nsteps) load_b(kb + 2, fill);
+    q2_step<MI, NG, NM, false>(smem_q2 + (kb & 1) * BUF, Xs, cur, acc);
+    __syncthreads();  // this step's buffer half and sums are no longer read
+    if (kb + 1 < nsteps) store_a((kb + 1) & 1, av);
+    __syncthreads();  // the next step's activation rows are in LDS
+  };
+  Q2Raw s0[NG][NM], s1[NG][NM], s2[NG][NM];
+  {
+    uint4 av[APT];
+    load_a(0, av);
+    load_b(0, s0);
+    if (nsteps > 1) load_b(1, s1);
+    store_a(0, av);
+    __syncthreads();
+  }
+  for (int kb = 0; kb < nsteps; kb += 3) {
+    step(kb, s0, s2);
+    if (kb + 1 < nsteps) step(kb + 1, s1, s0);
+    if (kb + 2 < nsteps) step(kb + 2, s2, s1);
+  }
+  // epilogue: lane holds rows 16 mi + 4 g + r of column n_w + 16 ng
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mrow = 16 * mi + 4 * g + r;
+      if (mrow >= valid) continue;
+      const size_t orow = size_t(a.perm[base + mrow]);
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        const int n = n_w + 16 * ng;
+        const float hf = silu(acc[mi][ng][0][r]) * acc[mi][ng][1][r];
+        const uint16_t hb = f32_to_bf16(hf);
+        a.h_out[orow * a.N + n] = hb;
+        a.h_lo_out[orow * a.N + n] = f32_to_bf16(hf - bf16_to_f32(hb));
+      }
+    }
+  }
+}
+
 template <bool GATEUP, int MI, int NG, bool ALO>
 static size_t q2_gemm_smem() {
   return size_t(2) * (ALO ? 2 : 1) * 16 * MI * LDS_ROW * 2 + size_t(16) * MI * XS_ROW * 2 + size_t(16) * MI * 4;
@@ -403,6 +541,22 @@ static hipError_t launch_q2_gemm(const GemmArgs &g, hipStream_t stream) {
   grid = (grid + 7) & ~7;
   BM_LAUNCH(GATEUP ? "routed_gateup_gemm_kernel" : "routed_down_gemm_kernel", (q2_gemm_kernel<GATEUP, MI, NG, ALO>),
             dim3(grid), dim3(256), smem, stream, g);
+  return hipGetLastError();
+}
+
+template <int MI, int NG>
+static hipError_t launch_q2_gemm_p3(const GemmArgs &g, hipStream_t stream) {
+  const size_t smem = q2_gemm_smem<true, MI, NG, false>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&q2_gemm_p3_kernel<MI, NG>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int grid = g.m_tiles * (g.N / (64 * NG));
+  grid = (grid + 7) & ~7;
+  BM_LAUNCH("routed_gateup_gemm_kernel", (q2_gemm_p3_kernel<MI, NG>), dim3(grid), dim3(256), smem, stream, g);
   return hipGetLastError();
 }
 
@@ -509,7 +663,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   g.b_expert_stride = q2_stride;
   g.h_out = a.h;
   g.h_lo_out = a.h_lo;
-  if ((err = launch_q2_gemm<true, GU_MI, GU_NG, false>(g, stream)) != hipSuccess) return err;
+  if ((err = launch_q2_gemm_p3<GU_MI, GU_NG>(g, stream)) != hipSuccess) return err;
   // routed down: A = h rows (hi + lo) by pair, N = D; tiles of 16 DN_MI pairs x 64 DN_NG rows
   g.tile_off = DN_MI == 4 ? p.tile_off : p.tile_off2;
   g.m_tiles = (P + 16 * DN_MI - 1) / (16 * DN_MI) + min(a.E, P);
