@@ -19,11 +19,11 @@
 //                       hi + mid + lo = w exactly.
 //  router_mfma_kernel   T > 8, bf16 x: logits = sum over the three parts of
 //                       x W_part^T on v_mfma_f32_16x16x32_bf16 (bf16 x bf16
-//                       products are exact in float32): 16 tokens x 64
+//                       products are exact in float32): 32 tokens x 64
 //                       experts per block, K split over its four waves, K
 //                       steps of 32 with the next step's operands loaded
 //                       ahead (each weight operand load is 1 KB of
-//                       contiguous bytes).
+//                       contiguous bytes and feeds two MFMAs).
 //  router_tile_kernel   T > 8, float32 x: 64 tokens x 64 experts per
 //                       256-thread block, K staged through LDS in steps of
 //                       32, 4x4 outputs per thread.
@@ -192,71 +192,78 @@ __global__ void __launch_bounds__(256) router_split_kernel(const float *__restri
 
 // Lane layout of v_mfma_f32_16x16x32_bf16: A lane l holds row l % 16 and k =
 // 8 (l / 16) + 0..7, B lane l column l % 16 and the same k, the result lane l
-// rows 4 (l / 16) + 0..3 of column l % 16.  A block computes 16 tokens x 64
+// rows 4 (l / 16) + 0..3 of column l % 16.  A block computes 32 tokens x 64
 // experts; its four waves take a quarter of K each (one step's loads in
-// flight ahead of its MFMAs: the K chain of a wave is what its latency
-// multiplies), and the partial sums are added in wave order through LDS.
-// Token rows past T read a clamped row, and neither they nor experts past E
-// are written.
+// flight ahead of its MFMAs), and the partial sums are added in wave order
+// through LDS.  Token rows past T read a clamped row, and neither they nor
+// experts past E are written.
 __global__ void __launch_bounds__(256) router_mfma_kernel(const uint16_t *__restrict__ x, int T, int D, int E,
                                                           const uint16_t *__restrict__ parts,
                                                           const float *__restrict__ bias,
                                                           float *__restrict__ logits) {
-  __shared__ float red[4][4][4][64];  // [wave][expert tile][row r][lane]
+  constexpr int MT = 2;                      // 16-token tiles per block (each weight operand feeds MT MFMAs)
+  __shared__ float red[4][MT][4][4][64];     // [wave][token tile][expert tile][row r][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 64;
+  const int t0 = blockIdx.x * 16 * MT, e0 = blockIdx.y * 64;
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int n_et = (E + 15) / 16, nks = D / 32, nq = nks / 4, ks0 = wave * nq;
-  const uint16_t *xa = x + size_t(min(t0 + r16, T - 1)) * D + kq;
+  const int n_et = (E + 15) / 16, nks = D / 32, nq = nks / 4, ks0 = wave * nq;  // nq is even (D >= 256)
+  const uint16_t *xa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) xa[mt] = x + size_t(min(t0 + 16 * mt + r16, T - 1)) * D + kq;
   // records of (part 0, expert tile e0/16 + n, step 0), this lane's 8 values
   const uint16_t *wb = parts + (size_t(e0 >> 4) * nks * 64 + lane) * 8;
   const size_t tile_stride = size_t(nks) * 512, part_stride = size_t(n_et) * tile_stride;
-  f32x4_t acc[4];
+  f32x4_t acc[MT][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint32_t A[4], B[4][3][4];
-  auto load = [&](int ks, uint32_t (&a)[4], uint32_t (&b)[4][3][4]) {
-    ld16(xa + 32 * ks, a);
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int ks, uint32_t (&a)[MT][4], uint32_t (&b)[4][3][4]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) ld16(xa[mt] + 32 * ks, a[mt]);
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int p = 0; p < 3; ++p) ld16(wb + p * part_stride + n * tile_stride + size_t(ks) * 512, b[n][p]);
   };
-  load(ks0, A, B);
-  for (int ks = ks0; ks < ks0 + nq; ++ks) {
-    uint32_t An[4], Bn[4][3][4];
-    const bool more = ks + 1 < ks0 + nq;
-    if (more) load(ks + 1, An, Bn);
+  auto mma = [&](const uint32_t (&a)[MT][4], const uint32_t (&b)[4][3][4]) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
 #pragma unroll
-      for (int p = 0; p < 3; ++p) acc[n] = mfma16(A, B[n][p], acc[n]);
-    if (more) {
+      for (int p = 0; p < 3; ++p)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) A[i] = An[i];
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) B[n][p][i] = Bn[n][p][i];
-    }
+        for (int mt = 0; mt < MT; ++mt) acc[mt][n] = mfma16(a[mt], b[n][p], acc[mt][n]);
+  };
+  // two register sets in turn, the loop unrolled by two so neither is copied
+  // (a copy would wait for the load in flight)
+  uint32_t A0[MT][4], B0[4][3][4], A1[MT][4], B1[4][3][4];
+  load(ks0, A0, B0);
+  for (int i = 0; i < nq; i += 2) {
+    load(ks0 + i + 1, A1, B1);
+    mma(A0, B0);
+    if (i + 2 < nq) load(ks0 + i + 2, A0, B0);
+    mma(A1, B1);
   }
 #pragma unroll
-  for (int n = 0; n < 4; ++n)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][n][r][lane] = acc[n][r];
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][mt][n][r][lane] = acc[mt][n][r];
   __syncthreads();
-  // wave w finishes expert tile w
+  // wave w finishes expert tile w of every token tile
   const int e = e0 + 16 * wave + r16;
   if (e >= E) return;
   const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = t0 + 4 * (lane >> 4) + r;
-    const float v = ((red[0][wave][r][lane] + red[1][wave][r][lane]) + red[2][wave][r][lane]) + red[3][wave][r][lane];
-    if (t < T) logits[int64_t(t) * E + e] = v + b;
-  }
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * mt + 4 * (lane >> 4) + r;
+      const float v = ((red[0][mt][wave][r][lane] + red[1][mt][wave][r][lane]) + red[2][mt][wave][r][lane]) +
+                      red[3][mt][wave][r][lane];
+      if (t < T) logits[int64_t(t) * E + e] = v + b;
+    }
 }
 
 size_t router_split_bytes(int E, int D) { return size_t(3) * ((E + 63) / 64 * 64) * D * 2; }
@@ -288,7 +295,7 @@ static hipError_t launch_logits(const void *x, bool xbf16, int T, int D, int E, 
               wr, E, D, wsplit);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 grid((T + 15) / 16, (E + 63) / 64);
+    const dim3 grid((T + 31) / 32, (E + 63) / 64);
     BM_LAUNCH("router_mfma_kernel", router_mfma_kernel, grid, dim3(256), 0, stream,
               static_cast<const uint16_t *>(x), T, D, E, wsplit, bias, logits);
   } else {
