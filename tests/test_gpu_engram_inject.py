@@ -75,7 +75,8 @@ def _compare(got, g_got, want, g_want, rows, w, res):
 
 
 @pytest.mark.parametrize("T,n_rows,W", [(1, 8, 4096), (5, 8, 4096), (13, 2, 256), (9, 24, 512),
-                                         (130, 2, 256), (1, 24, 5120), (5, 24, 5120), (37, 24, 5120)])
+                                         (16, 2, 256), (17, 4, 256), (64, 2, 512), (130, 2, 256),
+                                         (1, 24, 5120), (5, 24, 5120), (37, 24, 5120)])
 def test_inject_matches_oracle(T, n_rows, W):
     rows, w, qn, kn, res = _inputs(T, n_rows, W, 100 + T)
     mask = np.ones(T, dtype=bool)
@@ -107,3 +108,20 @@ def test_inject_on_gathered_engram_rows():
     got, g = _run(rows, w, qn, kn, 1e-6, res, None)
     want, gw = ei.inject(rows, w, qn.astype(np.float64), kn.astype(np.float64), 1e-6, res)
     _compare(got, g, want, gw, rows, w, res)
+
+
+def test_inject_large_batch_sampled_tokens():
+    # the real model's shape at a prefill-sized batch (64-token tiles and a
+    # ragged last tile): every position is computed on the device, the oracle
+    # recomputes a sample of them (positions are independent of each other)
+    T, n_rows, W = 1000, 24, 5120
+    rows, w, qn, kn, res = _inputs(T, n_rows, W, 9)
+    mask = np.ones(T, dtype=bool)
+    mask[[3, 700]] = False
+    got, g = _run(rows, w, qn, kn, 1e-6, res, mask)
+    idx = np.array([0, 1, 3, 63, 64, 127, 511, 700, 959, 960, 999])
+    want, gw = ei.inject(rows[idx], w, qn.astype(np.float64), kn.astype(np.float64), 1e-6, res[idx],
+                         mask=mask[idx])
+    _compare(got[idx], g[idx], want, gw, rows[idx], w, res[idx])
+    for t in (3, 700):
+        assert np.array_equal(got[t], res[t]) and g[t].tolist() == [0.0] * 4
