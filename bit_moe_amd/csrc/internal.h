@@ -1,21 +1,27 @@
 // Launch functions of the kernel translation units (internal to libbitmoe).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace bm {
 
-// Launch-timing hooks (no-ops unless bitmoe_profile_start() was called).
-void prof_begin(const char *name, hipStream_t stream);
-void prof_end(hipStream_t stream);
+// Launch timing (off unless bitmoe_profile_start() was called): prof_events
+// hands out a start/stop event pair for the launch, or nulls when timing is
+// off.  The pair goes to hipExtLaunchKernel, which stamps it from the kernel's
+// own dispatch (start and end of its execution, no queue gaps).
+void prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
 
-#define BM_LAUNCH(name, kernel, grid, block, shmem, stream, ...)               \
-  do {                                                                         \
-    ::bm::prof_begin(name, stream);                                            \
-    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
-    ::bm::prof_end(stream);                                                    \
+#define BM_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                                        \
+  do {                                                                                                  \
+    hipEvent_t bm_ev_a_ = nullptr, bm_ev_b_ = nullptr;                                                  \
+    ::bm::prof_events(name, &bm_ev_a_, &bm_ev_b_);                                                      \
+    if (bm_ev_a_)                                                                                       \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, bm_ev_a_, bm_ev_b_, 0u, __VA_ARGS__);   \
+    else                                                                                                \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                              \
   } while (0)
 
 hipError_t launch_engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n,

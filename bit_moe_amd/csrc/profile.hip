@@ -1,5 +1,6 @@
-// Optional per-kernel launch timing with HIP events recorded on the launch
-// stream (off unless bitmoe_profile_start() was called).
+// Optional per-kernel launch timing (off unless bitmoe_profile_start() was
+// called): every launch gets a start/stop event pair that hipExtLaunchKernel
+// stamps with the kernel's own execution start and end.
 #include <string.h>
 
 #include <mutex>
@@ -28,7 +29,6 @@ bool g_on = false;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 std::vector<Agg> g_aggs;
-thread_local int g_open = -1;
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -43,21 +43,14 @@ hipEvent_t take_event() {
 
 }  // namespace
 
-void prof_begin(const char *name, hipStream_t stream) {
+void prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop) {
   if (!g_on) return;
   std::lock_guard<std::mutex> lk(g_mu);
   Rec r{name, take_event(), take_event()};
   if (!r.a || !r.b) return;
-  hipEventRecord(r.a, stream);
   g_recs.push_back(r);
-  g_open = int(g_recs.size()) - 1;
-}
-
-void prof_end(hipStream_t stream) {
-  if (!g_on || g_open < 0) return;
-  std::lock_guard<std::mutex> lk(g_mu);
-  hipEventRecord(g_recs[g_open].b, stream);
-  g_open = -1;
+  *start = r.a;
+  *stop = r.b;
 }
 
 }  // namespace bm

@@ -430,3 +430,32 @@ def test_prefill_chunk_sampled_tokens():
     xv = ld.x_values()[sample]
     ref = moe.moe_layer(ol, xv, bias=ld.bias(), ids=ids_h[sample])
     assert compare.max_rel_error(yv[sample], ref.out) < TOL
+
+
+# ------------------------------------------------------------------ launch timing
+
+
+def test_profiled_launches_give_identical_results_and_timings():
+    # with timing on, every kernel is launched through hipExtLaunchKernel with
+    # its event pair: the outputs must not change, and every kernel of the
+    # decode layer is counted once per call with a positive duration
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 12)
+    layer = device_layer(ld)
+    x = x_device(ld, 3, 1)
+    ws = bm.workspace(layer, 1)
+    ids0, w0 = bm.route(layer, x, ws)
+    y0 = bm.expert_ffn(layer, x, ids0, w0, ws).clone()
+    torch.cuda.synchronize()
+    bm.profile_start()
+    ids1, w1 = bm.route(layer, x, ws)
+    y1 = bm.expert_ffn(layer, x, ids1, w1, ws)
+    torch.cuda.synchronize()
+    prof = bm.profile_stop()
+    assert torch.equal(ids0, ids1) and torch.equal(w0.view(torch.int32), w1.view(torch.int32))
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+    for name in ("router_gemv_kernel", "topk_kernel", "ffn_gateup_kernel", "ffn_down_kernel", "combine_kernel"):
+        ms, n = prof[name]
+        assert n == 1 and 0.0 < ms < 50.0, (name, ms, n)
+    # timing off again: nothing more is recorded
+    bm.profile_start()
+    assert bm.profile_stop() == {}
