@@ -76,7 +76,8 @@ def _compare(got, g_got, want, g_want, rows, w, res):
 
 @pytest.mark.parametrize("T,n_rows,W", [(1, 8, 4096), (5, 8, 4096), (13, 2, 256), (9, 24, 512),
                                          (16, 2, 256), (17, 4, 256), (64, 2, 512), (130, 2, 256),
-                                         (1, 24, 5120), (5, 24, 5120), (37, 24, 5120)])
+                                         (1, 24, 5120), (5, 24, 5120), (37, 24, 5120),
+                                         (1, 32, 8192), (20, 32, 8192)])  # largest rows and width
 def test_inject_matches_oracle(T, n_rows, W):
     rows, w, qn, kn, res = _inputs(T, n_rows, W, 100 + T)
     mask = np.ones(T, dtype=bool)
@@ -125,3 +126,12 @@ def test_inject_large_batch_sampled_tokens():
     _compare(got[idx], g[idx], want, gw, rows[idx], w, res[idx])
     for t in (3, 700):
         assert np.array_equal(got[t], res[t]) and g[t].tolist() == [0.0] * 4
+
+
+def test_inject_every_position_masked():
+    # the projection still runs (wide kernel at T = 20); no residual element
+    # changes and every gate reads 0
+    T, n_rows, W = 20, 2, 256
+    rows, w, qn, kn, res = _inputs(T, n_rows, W, 31)
+    got, g = _run(rows, w, qn, kn, 1e-6, res, np.zeros(T, dtype=bool))
+    assert np.array_equal(got, res) and not g.any()
