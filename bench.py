@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -89,37 +91,82 @@ def stored_traffic(kernel_src: str, label: str):
     return float(vals["traffic_bytes"])
 
 
+def _host_cpu() -> dict:
+    """Host threads available to this process and the CPU model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "model": model}
+
+
+def _oracle_pass(moe, cfg, ld, x, bias=None):
+    """One timed pass of the whole fp64 layer on tokens x.  A fresh oracle
+    Layer per pass (its matrix memo starts empty), so every selected expert's
+    three matrices and the shared expert are dequantised inside the timed
+    region, as the layer must; the raw input bytes are generated before."""
+    ids, _, _ = moe.route(x, ld.router(), cfg.top_k, bias)
+    raw = {(kd, int(e)): ld.expert_bytes(kd, int(e)) for e in np.unique(ids) for kd in ("gate", "up", "down")}
+    sh = {kd: ld.shared_bytes(kd) for kd in ("gate", "up", "down")}
+    layer = moe.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, ld.router(), lambda kd, e: raw[(kd, e)],
+                      lambda kd: sh[kd])
+    t0 = time.perf_counter()
+    moe.moe_layer(layer, x, bias=bias)
+    return time.perf_counter() - t0, len(np.unique(ids))
+
+
 def cpu_baseline(seed: int, n_tokens: int, repeats: int) -> dict:
-    """The fp64 oracle on the host for a bounded sample of decode tokens: each
-    token's whole layer is computed `repeats` times on the same inputs (the
-    inputs are generated before timing and the oracle caches nothing, so every
-    repeat does the full work)."""
+    """The fp64 oracle on the host for bounded samples.  Headline: decode
+    tokens (the single-layer T=1 workload), each token one full layer pass
+    (router, its 6 experts dequantised + SwiGLU FFN, the Q8_0 shared expert
+    dequantised + FFN, combine) `repeats` times with a fresh oracle layer per
+    pass, so nothing carries over between passes.  Beside it: one verify
+    batch (T=5, the union of its experts) and a sample of prefill-chunk tokens
+    (Zipf-biased routing), timed the same way.  BLAS may use every host
+    thread; NumPy's elementwise work (most of the dequantisation) runs on
+    one."""
     import threadpoolctl
 
     import synthdata
     from oracle import moe
 
-    cfg = synthdata.CONFIGS["decode"]
-    ld = synthdata.LayerData(cfg, seed, 0)
-    sh = {kd: ld.shared_bytes(kd) for kd in ("gate", "up", "down")}
-    total = 0.0
-    for t in range(n_tokens):
-        x = ld.x_values(10_000 + t, 1)
-        ids, _, _ = moe.route(x, ld.router(), cfg.top_k)
-        # the layer's inputs (selected experts' bytes) are generated before timing
-        cache = {(kd, int(e)): ld.expert_bytes(kd, int(e)) for e in ids[0] for kd in ("gate", "up", "down")}
-        layer = moe.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, ld.router(),
-                          lambda kd, e: cache[(kd, e)], lambda kd: sh[kd])
-        with threadpoolctl.threadpool_limits(limits=1):  # one core, stated below
+    host = _host_cpu()
+    with threadpoolctl.threadpool_limits(limits=host["nproc"]):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+        cfg = synthdata.CONFIGS["decode"]
+        ld = synthdata.LayerData(cfg, seed, 0)
+        total = 0.0
+        for t in range(n_tokens):
+            x = ld.x_values(10_000 + t, 1)
             for _ in range(repeats):
-                t0 = time.perf_counter()
-                moe.moe_layer(layer, x)
-                total += time.perf_counter() - t0
-    n = n_tokens * repeats
-    return {"value": round(n / total, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tokens} decode tokens of layer instance 0, each through the whole fp64 layer (router, "
-                      f"6 experts dequantised + SwiGLU FFN, Q8_0 shared expert, combine) {repeats} times: "
-                      f"{n} layer passes in {total:.1f} s on one core"}
+                dt, _ = _oracle_pass(moe, cfg, ld, x)
+                total += dt
+        n = n_tokens * repeats
+        vcfg = synthdata.CONFIGS["verify"]
+        vld = synthdata.LayerData(vcfg, seed, 0)
+        v_dt, v_u = _oracle_pass(moe, vcfg, vld, vld.x_values(20_000, 5))
+        pcfg = synthdata.CONFIGS["prefill"]
+        pld = synthdata.LayerData(pcfg, seed, 0)
+        n_pf = 4
+        p_dt, p_u = _oracle_pass(moe, pcfg, pld, pld.x_values()[np.linspace(0, pcfg.T - 1, n_pf).astype(int)],
+                                 bias=pld.bias())
+    return {"value": round(n / total, 4), "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "host": host,
+            "sample": f"{n_tokens} decode tokens (T=1, layer instance 0), each through the whole fp64 layer "
+                      f"(router, 6 experts dequantised + SwiGLU FFN, Q8_0 shared expert, combine) {repeats} "
+                      f"time(s) with a fresh oracle layer per pass: {n} layer passes in {total:.1f} s; BLAS on "
+                      f"{blas_threads} thread(s) of {host['nproc']}, elementwise NumPy on one",
+            "verify_T5": {"tokens_per_s": round(5 / v_dt, 4), "s_per_step": round(v_dt, 2), "experts": v_u,
+                          "sample": "one verify batch of 5 tokens through the whole fp64 layer"},
+            "prefill_sample": {"tokens_per_s": round(n_pf / p_dt, 4), "s": round(p_dt, 2), "experts": p_u,
+                               "sample": f"{n_pf} tokens spread over the 4096-token chunk (Zipf-biased "
+                                         f"routing) through the whole fp64 layer; a full chunk would "
+                                         f"dequantise every expert once and is not timed"}}
 
 
 def make_layer(bm, torch, synthdata, cfg, seed: int, layer: int, lut, dev):
@@ -513,7 +560,7 @@ def main() -> int:
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-tokens", type=int, default=4)
-    ap.add_argument("--cpu-repeats", type=int, default=60)
+    ap.add_argument("--cpu-repeats", type=int, default=1)
     ap.add_argument("--verify-steps", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -22,7 +22,8 @@ OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
 MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_DECODE_INT8 = 0, 1, 2, 3
-DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN = 1, 2, 4
+DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN, DEV_DUP_EXPERT = 1, 2, 4, 8
+LAYOUT_CANONICAL = 0
 SCORE_SOFTMAX, SCORE_SQRT_SOFTPLUS = 0, 1
 FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
 
@@ -45,6 +46,7 @@ class _LayerC(ctypes.Structure):
     _fields_ = [
         ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("n_experts", ctypes.c_int32),
         ("top_k", ctypes.c_int32), ("wfmt", ctypes.c_int32), ("shared_wfmt", ctypes.c_int32),
+        ("layout_flags", ctypes.c_int32),
         ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
         ("w_router", ctypes.c_void_p), ("ws_gate", ctypes.c_void_p), ("ws_up", ctypes.c_void_p),
         ("ws_down", ctypes.c_void_p),
@@ -158,11 +160,12 @@ class Layer:
     ws_gate: Optional[torch.Tensor] = None
     ws_up: Optional[torch.Tensor] = None
     ws_down: Optional[torch.Tensor] = None
+    layout_flags: int = LAYOUT_CANONICAL
 
     def c(self) -> _LayerC:
         shared = self.ws_gate is not None
         return _LayerC(self.d_model, self.d_ff, self.n_experts, self.top_k, WFMT_Q2SB,
-                       WFMT_Q8_0 if shared else WFMT_NONE,
+                       WFMT_Q8_0 if shared else WFMT_NONE, self.layout_flags,
                        self.w_gate.data_ptr(), self.w_up.data_ptr(), self.w_down.data_ptr(),
                        self.w_router.data_ptr(),
                        self.ws_gate.data_ptr() if shared else None,

@@ -33,6 +33,9 @@ int check_layer(const char *fn, const bitmoe_layer *L) {
   if (!L) return fail(BITMOE_EINVAL, "%s: layer is NULL", fn);
   if (L->wfmt != BITMOE_WFMT_Q2SB)
     return fail(BITMOE_EUNSUPPORTED, "%s: routed weight format %d is not Q2SB (%d)", fn, L->wfmt, BITMOE_WFMT_Q2SB);
+  if (L->layout_flags != BITMOE_LAYOUT_CANONICAL)
+    return fail(BITMOE_EUNSUPPORTED, "%s: layout_flags %d: only the canonical block layout (0) is implemented", fn,
+                L->layout_flags);
   if (L->shared_wfmt != BITMOE_WFMT_NONE && L->shared_wfmt != BITMOE_WFMT_Q8_0)
     return fail(BITMOE_EUNSUPPORTED, "%s: shared weight format %d is neither NONE nor Q8_0", fn, L->shared_wfmt);
   if (!pow2(L->d_model) || L->d_model < 256 || L->d_model > 4096)

@@ -158,4 +158,16 @@ BM_DEVICE void record_fault(int64_t *status, int64_t flag, int64_t index) {
             (unsigned long long)(INT64_MAX - index));
 }
 
+// Status flags (the values of BITMOE_DEV_* in the public header).
+constexpr int64_t FAULT_BAD_EXPERT = 1, FAULT_BAD_ROW = 2, FAULT_BAD_TOKEN = 4, FAULT_DUP_EXPERT = 8;
+
+// A pair (t, j) is served only if its expert id e lies in [0, E) and no
+// earlier slot j' < j of the same token holds e: a token that names an expert
+// twice gets that expert once, at its first slot.  row = the token's k ids.
+BM_DEVICE bool repeats_earlier(const int32_t *row, int j, int e) {
+  for (int i = 0; i < j; ++i)
+    if (row[i] == e) return true;
+  return false;
+}
+
 }  // namespace bm

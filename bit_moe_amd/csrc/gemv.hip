@@ -1078,7 +1078,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
     if (j >= k) break;
     const int e = ids[t * k + j];
     if (e < 0 || e >= E) {
-      if (c == 0) record_fault(status, 1, int64_t(t) * k + j);
+      if (c == 0) record_fault(status, FAULT_BAD_EXPERT, int64_t(t) * k + j);
+      continue;
+    }
+    if (repeats_earlier(ids + t * k, j, e)) {  // served once, at its first slot
+      if (c == 0) record_fault(status, FAULT_DUP_EXPERT, int64_t(t) * k + j);
       continue;
     }
     const float w = wts[t * k + j];

@@ -9,7 +9,8 @@
 //
 // Three kernels over chunks of 64 tokens (one wave per chunk):
 //  plan_count    per-chunk expert histogram (LDS atomics: counts are
-//                order-independent)
+//                order-independent); out-of-range ids and repeats of an
+//                expert within a token are left out and recorded
 //  plan_scan     one block: per-expert prefix over chunks, exclusive scan over
 //                experts, union compaction, GEMM tile offsets
 //  plan_scatter  per chunk, the tokens in order: each pair takes the next
@@ -29,12 +30,15 @@ __global__ void __launch_bounds__(64) plan_count_kernel(const int32_t *__restric
   __syncthreads();
   const int t = chunk * 64 + threadIdx.x;
   if (t < T) {
+    const int32_t *row = ids + int64_t(t) * k;
     for (int j = 0; j < k; ++j) {
-      const int e = ids[int64_t(t) * k + j];
-      if (e >= 0 && e < E)
-        atomicAdd(&hist[e], 1);
+      const int e = row[j];
+      if (e < 0 || e >= E)
+        record_fault(status, FAULT_BAD_EXPERT, int64_t(t) * k + j);
+      else if (repeats_earlier(row, j, e))
+        record_fault(status, FAULT_DUP_EXPERT, int64_t(t) * k + j);
       else
-        record_fault(status, 1, int64_t(t) * k + j);
+        atomicAdd(&hist[e], 1);
     }
   }
   __syncthreads();
@@ -105,14 +109,15 @@ __global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restr
   for (int e = threadIdx.x; e < E; e += 64) s_pos[e] = p.offsets[e] + p.chunk_counts[int64_t(chunk) * E + e];
   for (int i = threadIdx.x; i < nt * k; i += 64) s_ids[i] = ids[int64_t(t0) * k + i];
   __syncthreads();
-  // tokens of the chunk in order, lane j taking slot j: a token chooses an
-  // expert at most once, so the k lanes of a step advance distinct counters
-  // and each expert's pairs land in token order (stable)
+  // tokens of the chunk in order, lane j taking slot j: the pairs served are
+  // those of plan_count (in range, first slot of their expert in the token),
+  // so the k lanes of a step advance distinct counters and each expert's
+  // pairs land in token order (stable)
   const int j = threadIdx.x;
   if (j >= k) return;
   for (int u = 0; u < nt; ++u) {
     const int e = s_ids[u * k + j];
-    if (e < 0 || e >= E) continue;
+    if (e < 0 || e >= E || repeats_earlier(s_ids + u * k, j, e)) continue;
     const int pos = s_pos[e];
     s_pos[e] = pos + 1;
     p.perm[pos] = (t0 + u) * k + j;

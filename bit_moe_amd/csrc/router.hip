@@ -459,13 +459,20 @@ BM_DEVICE void topk_variant_token(const float *L, int E, int k, int score, const
     }
   }
   // unbiased scores of the selection, renormalised
+  // (a table row may name an expert outside [0, E) or repeat one: such slots
+  // get weight 0 and are recorded; the top-k selection never does either)
   float g[8], gs = 0.f;
   for (int j = 0; j < k; ++j) {
     const int e = sel[j];
     const bool ok = e >= 0 && e < E;
-    g[j] = ok ? slot_value<PER>(sc, e & 63, e >> 6) : 0.f;
+    bool dup = false;
+    for (int i = 0; i < j; ++i) dup = dup || (ok && sel[i] == e);
+    g[j] = ok && !dup ? slot_value<PER>(sc, e & 63, e >> 6) : 0.f;
     gs += g[j];
-    if (!ok && hrow && lane == 0) record_fault(status, 1, pair0 + j);
+    if (hrow && lane == 0) {
+      if (!ok) record_fault(status, FAULT_BAD_EXPERT, pair0 + j);
+      else if (dup) record_fault(status, FAULT_DUP_EXPERT, pair0 + j);
+    }
   }
   if (lane == 0) {
     const float inv = gs > 0.f ? 1.0f / gs : 0.f;
@@ -494,7 +501,7 @@ __global__ void __launch_bounds__(256) topk_variant_kernel(const float *__restri
         ids[int64_t(t) * k + lane] = -1;
         wts[int64_t(t) * k + lane] = 0.f;
       }
-      if (lane == 0) record_fault(status, 4, t);
+      if (lane == 0) record_fault(status, FAULT_BAD_TOKEN, t);
       return;
     }
     hrow = htab + id * k;

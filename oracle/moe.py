@@ -165,8 +165,13 @@ def route_variant(x, w_router, k: int, logit_bias=None, select_bias=None, score:
         ids = np.asarray(hash_ids, dtype=np.int64)
     else:
         ids = topk_ids(sel, k)
-    g = np.take_along_axis(sc, ids, axis=1)
-    return ids, g / g.sum(axis=1, keepdims=True), L, sel
+    # a table row may name an expert outside [0, E) or repeat one: such slots
+    # are not served (see served_pairs) and get weight 0; the row's weights
+    # are renormalised over the slots that are
+    keep = served_pairs(ids, L.shape[1])
+    g = np.where(keep, np.take_along_axis(sc, np.clip(ids, 0, L.shape[1] - 1), axis=1), 0.0)
+    tot = g.sum(axis=1, keepdims=True)
+    return ids, np.divide(g, tot, out=np.zeros_like(g), where=tot > 0), L, sel
 
 
 # ---------------------------------------------------------------- plan
@@ -184,19 +189,44 @@ class Plan:
         return int(self.union.size)
 
 
+def served_pairs(ids: np.ndarray, n_experts: int) -> np.ndarray:
+    """Which (token, slot) pairs are served, bool [T][k].  [Reading: the pages
+    route a token to k distinct experts and do not say what a selection that
+    names an expert twice (a hand-written hash-routing table row, a caller's
+    ids) means.  Taken here: the token gets that expert once, at its first
+    slot; a later slot naming it again, or an id outside [0, E), contributes
+    nothing and is reported.]"""
+    ids = np.atleast_2d(np.asarray(ids, dtype=np.int64))
+    T, k = ids.shape
+    ok = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < n_experts and e not in seen:
+                ok[t, j] = True
+            seen.add(e)
+    return ok
+
+
 def plan(ids: np.ndarray, n_experts: int) -> Plan:
-    """Step 3.  Pairs are numbered p = t*k + j; ``perm`` lists them grouped by
-    expert in ascending expert order, and in ascending p inside a group."""
+    """Step 3.  Pairs are numbered p = t*k + j; ``perm`` lists the served
+    pairs (:func:`served_pairs`) grouped by expert in ascending expert order,
+    and in ascending p inside a group."""
     flat = np.asarray(ids, dtype=np.int64).reshape(-1)
+    keep = served_pairs(ids, n_experts).reshape(-1)
     counts = np.zeros(n_experts, dtype=np.int64)
-    for e in flat:
-        counts[e] += 1
+    for p, e in enumerate(flat):
+        if keep[p]:
+            counts[e] += 1
     offsets = np.zeros(n_experts + 1, dtype=np.int64)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
-    perm = np.empty(flat.size, dtype=np.int64)
+    perm = np.empty(int(offsets[-1]), dtype=np.int64)
     fill = offsets[:-1].copy()
     for p, e in enumerate(flat):
+        if not keep[p]:
+            continue
         perm[fill[e]] = p
         fill[e] += 1
     union = np.array([e for e in range(n_experts) if counts[e] > 0], dtype=np.int64)

@@ -67,6 +67,7 @@ def test_workspace_size_valid_layer(lib):
     ("n_experts", 0, bm.EUNSUPPORTED), ("n_experts", 2000, bm.EUNSUPPORTED), ("top_k", 0, bm.EINVAL),
     ("top_k", 9, bm.EINVAL), ("wfmt", 7, bm.EUNSUPPORTED), ("shared_wfmt", 5, bm.EUNSUPPORTED),
     ("w_gate", 0, bm.EINVAL), ("w_up", 0x10004, bm.EINVAL), ("w_router", 0, bm.EINVAL), ("ws_down", 0, bm.EINVAL),
+    ("layout_flags", 1, bm.EUNSUPPORTED), ("layout_flags", -1, bm.EUNSUPPORTED),
 ])
 def test_layer_validation(lib, field, value, code):
     rc, _ = _ws_size(lib, _layer(**{field: value}), 1)

@@ -121,3 +121,45 @@ def test_int8_ffn_single_expert_matches_dense_int8_route():
     ysh = int8_mode.ffn_int8(layer, -1, x[t])[0]
     out = sum(w * yy for w, yy in zip(res.weights[t], y)) + ysh
     assert np.allclose(res.out[t], out, rtol=1e-12, atol=1e-12 * np.abs(out).max())
+
+
+def _q2_block(codes: dict, sc0: int, d_bits: int) -> np.ndarray:
+    """One 84-byte Q2 super-block: sub-block 0 scale sc0 (min 0), the given
+    {weight index: code}, fp16 d = d_bits, dmin = 0."""
+    blk = np.zeros(84, np.uint8)
+    blk[0] = sc0
+    for i, q in codes.items():
+        byte, shift = formats.q2_code_location(i)
+        blk[byte] |= q << shift
+    blk[80], blk[81] = d_bits & 0xFF, d_bits >> 8
+    return blk
+
+
+def test_ffn_int8_requantises_h_hand_worked():
+    # d_model = d_ff = 256, one expert, x = 127 everywhere: x quantises
+    # exactly (d = 1, q = 127).  Gate rows 0 and 1 have weight 0 = 2^-10 (d =
+    # 2^-10 = fp16 0x1400, sc 1, code 1): g = 127/1024 for both.  Up row 0 has
+    # code 3 at weight 0 (u = 381/1024), up row 1 code 1 (u = 127/1024); all
+    # other rows are zero, so h = silu(127/1024) * (3, 1, 0, ...) * 127/1024.
+    # h quantises in block 0 with d_h = fp32(h_0/127): q_0 = 127 and
+    # q_1 = rint(127/3) = rint(42.33) = 42.  Down row 0 has weights 1 at
+    # columns 0 and 1 (d = 1.0 = 0x3C00, sc 1, code 1), the other rows zero:
+    # y_0 = d_h * (127 + 42) = 169 d_h, where the unquantised h would give
+    # h_0 + h_1 = 169.33 d_h.
+    D = F = 256
+    zero = np.zeros(84, np.uint8)
+    gate = np.concatenate([_q2_block({0: 1}, 1, 0x1400)] * 2 + [zero] * (F - 2))
+    up = np.concatenate([_q2_block({0: 3}, 1, 0x1400), _q2_block({0: 1}, 1, 0x1400)] + [zero] * (F - 2))
+    down = np.concatenate([_q2_block({0: 1, 1: 1}, 1, 0x3C00)] + [zero] * (D - 1))
+    mats = {"gate": gate, "up": up, "down": down}
+    layer = moe.Layer(D, F, 1, 1, np.zeros((1, D), np.float32), lambda kind, e: mats[kind])
+    y, h = int8_mode.ffn_int8(layer, 0, np.full(D, 127.0, np.float32))
+    g = 127 / 1024
+    s = g / (1 + math.exp(-g))
+    h0 = s * 381 / 1024
+    assert math.isclose(h[0], h0, rel_tol=1e-15) and math.isclose(h[1], h0 / 3, rel_tol=1e-15)
+    assert np.all(h[2:] == 0)
+    d_h = float(np.float32(np.float32(h0) / np.float32(127)))
+    assert math.isclose(y[0], 169 * d_h, rel_tol=1e-12), (y[0], 169 * d_h)
+    assert abs(y[0] - (h0 + h0 / 3)) > 1e-3 * abs(y[0])  # h is not used unquantised
+    assert np.all(y[1:] == 0)

@@ -170,6 +170,22 @@ def test_forced_selection_weights():
     assert np.allclose(res.out, res2.out, rtol=1e-12, atol=1e-12)
 
 
+def test_residual_rescale_hand_worked():
+    # r = x + out per token row, x' = bf16(r / sqrt(mean(r^2) + 1e-6)), worked by hand:
+    # row 0: r = (1, 1), mean 1: 1/sqrt(1.000001) = 0.9999995 -> bf16 1.0 = 0x3F80 twice
+    # row 1: r = (3, 4), mean 12.5, rms = 3.5355339: 0.848528 -> 217/256 = 0x3F59,
+    #        1.131371 -> 145/128 = 0x3F91 (steps 2^-8 below 1, 2^-7 above)
+    # (dropping x gives (0, 1.414) = (0x0000, 0x3FB5); x - out flips the second sign)
+    x = np.array([[1.0, 0.0], [3.0, 0.0]])
+    out = np.array([[0.0, 1.0], [0.0, 4.0]])
+    assert moe.residual_rescale(x, out).tolist() == [[0x3F80, 0x3F80], [0x3F59, 0x3F91]]
+    # tiny rows: eps matters.  r = (2^-10, 2^-10), mean r^2 = 2^-20, so
+    # r/rms = 1/sqrt(1 + 1e-6 * 2^20) = 1/sqrt(2.048576) = 0.698673 -> 179/256 = 0x3F33
+    # (eps = 0 would give 1.0 = 0x3F80, eps = 1e-5 gives 0.29507 = 0x3E97)
+    tiny = np.full((1, 2), 2.0 ** -10)
+    assert moe.residual_rescale(tiny, np.zeros((1, 2))).tolist() == [[0x3F33, 0x3F33]]
+
+
 def test_residual_rescale_unit_rms():
     rng = np.random.default_rng(6)
     x = rng.normal(size=(3, 4096))
@@ -177,3 +193,41 @@ def test_residual_rescale_unit_rms():
     bits = moe.residual_rescale(x, out)
     v = formats.bf16_to_f64(bits)
     assert np.allclose(np.sqrt(np.mean(v * v, axis=1)), 1.0, rtol=1e-2)
+
+
+# ------------------------------------------------------------------ repeated experts
+
+
+def test_served_pairs_hand_cases():
+    ids = np.array([[0, 1, 0, 3], [2, 2, 2, 2], [5, -1, 4, 1], [3, 1, 1, 0]])
+    want = [[1, 1, 0, 1], [1, 0, 0, 0], [0, 0, 1, 1], [1, 1, 0, 1]]
+    assert moe.served_pairs(ids, 5).astype(int).tolist() == want
+
+
+def test_plan_leaves_out_repeats_and_bad_ids():
+    ids = np.array([[0, 1, 0], [1, 1, 2], [7, 2, 0]])
+    pl = moe.plan(ids, 3)
+    # served pairs: 0 (e0), 1 (e1), 3 (e1), 5 (e2), 7 (e2), 8 (e0)
+    assert pl.counts.tolist() == [2, 2, 2]
+    assert pl.perm.tolist() == [0, 8, 1, 3, 5, 7]
+    assert pl.union.tolist() == [0, 1, 2]
+
+
+def test_repeated_expert_contributes_once():
+    # a token that names expert e twice gets FFN_e once, at its first slot:
+    # the later slot's output is zero, the others equal a selection without
+    # the repeat
+    ld, layer = _tiny_layer(seed=4)
+    x = ld.x_values()[:2]
+    dup = np.array([[3, 5], [7, 7]])
+    alt = np.array([[3, 5], [7, 8]])
+    y_dup = moe.expert_outputs(layer, x, dup)
+    y_alt = moe.expert_outputs(layer, x, alt)
+    assert np.all(y_dup[1, 1] == 0)
+    assert np.array_equal(y_dup[0], y_alt[0]) and np.array_equal(y_dup[1, 0], y_alt[1, 0])
+    # hash-routed rows: the repeated entry gets weight 0, the others share 1
+    xv = ld.x_values()[:1]
+    ids, w, L, _ = moe.route_variant(xv, layer.w_router, 2, hash_ids=np.array([[6, 6]]))
+    assert w.tolist() == [[1.0, 0.0]]
+    ids, w, L, _ = moe.route_variant(xv, layer.w_router, 2, hash_ids=np.array([[16, 6]]))  # E = 16
+    assert w.tolist() == [[0.0, 1.0]]
