@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "bitmoe.h"
 #include "internal.h"
 
@@ -87,7 +89,7 @@ struct DecodeWs {
 struct PrefillWs {
   bm::PlanBufs plan;
   int32_t *tile_off, *tile_off2;
-  uint16_t *xs, *h, *hs, *h_lo, *hs_lo, *sw;
+  uint16_t *xs, *h, *hs, *h_lo, *hs_lo, *sw, *xsum;
   float *y, *ys;
 };
 
@@ -184,6 +186,8 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   w->sw = static_cast<uint16_t *>(c.take(shared ? size_t(3) * L->d_ff * L->d_model * (2 + 4 / 32.0) : 0));
   w->y = static_cast<float *>(c.take(P * L->d_model * 4));
   w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
+  // sub-block sums of the grouped GEMMs' activation rows: 32 bf16 per row and 256 columns
+  w->xsum = static_cast<uint16_t *>(c.take(std::max(size_t(T) * L->d_model, P * L->d_ff) / 256 * 32 * 2));
 }
 
 size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
@@ -373,6 +377,7 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   a.h_lo = w.h_lo;
   a.hs_lo = w.hs_lo;
   a.sw_bf16 = w.sw;
+  a.xsum = w.xsum;
   a.y = w.y;
   a.ys = w.ys;
   a.out = y;

@@ -106,14 +106,15 @@ struct PrefillArgs {
   const int32_t *ids;
   const float *wts;
   PlanBufs plan;
-  int32_t *tile_off;   // [E+1] M-tiles of PREFILL_BM tokens per expert, prefix
-  int32_t *tile_off2;  // [E+1] M-tiles of PREFILL_BM_DOWN pairs per expert, prefix
+  int32_t *tile_off;   // [E+1] chunks of PREFILL_BM tokens per expert, prefix
+  int32_t *tile_off2;  // [E+1] chunks of PREFILL_BM_DOWN pairs per expert, prefix
   uint16_t *xs;        // [T][D] bf16 copy of x (x_f32 only)
   uint16_t *h;         // [T*k][F] bf16 hi part of h, pair order
   uint16_t *hs;        // [T][F] bf16 hi part (shared expert)
   uint16_t *h_lo;      // lo parts
   uint16_t *hs_lo;
   uint16_t *sw_bf16;   // [3][F*D] bf16 copy of the shared expert (gate, up, down)
+  uint16_t *xsum;      // activation sub-block sums of the grouped GEMMs: max(T*D, T*k*F) / 8 bf16
   float *y;            // [T*k][D] float32, pair order
   float *ys;           // [T][D]
   void *out;
@@ -121,9 +122,12 @@ struct PrefillArgs {
   int64_t *status;
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
+// routed grouped GEMM (gate/up with h out, or down with y out) over the plan's
+// chunks, after the activation rows' sub-block sums (into sums)
+hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, hipStream_t stream);
 hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,
                                    hipStream_t stream);
-constexpr int PREFILL_BM = 64;       // tokens per M-tile of the gate/up grouped GEMM
-constexpr int PREFILL_BM_DOWN = 32;  // pairs per M-tile of the down grouped GEMM
+constexpr int PREFILL_BM = 48;       // tokens per chunk of the gate/up grouped GEMM (tile_off)
+constexpr int PREFILL_BM_DOWN = 32;  // pairs per chunk of the down grouped GEMM (tile_off2)
 
 }  // namespace bm
