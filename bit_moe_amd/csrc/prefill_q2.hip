@@ -120,22 +120,32 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
   if constexpr (GATEUP) wb[1] = g.b1 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
   // copies of step kb into buffer half: activation rows (512 B each, half a
   // wave per row; this wave's rows wave, wave + W, ..) and their sums (64 B
-  // per row, 16 rows per instruction)
-  auto issue = [&](int kb, int half) {
-    uint8_t *ad = abuf + half * Gm::BUF;
-    for (int i = wave; i < PARTS * 16 * NT; i += W) {
+  // per row, 16 rows per instruction).  The row bases are wave-uniform and
+  // stay in scalar registers.
+  constexpr int NA = PARTS * 16 * NT, JA = (NA + W - 1) / W;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t *asrc[JA];
+  uint32_t adst[JA];
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int i = wv + W * j;
+    asrc[j] = nullptr;
+    adst[j] = 0;
+    if (i < NA) {
       const int part = i / (16 * NT), r = i % (16 * NT);
-      const int src = rows[r];
-      if (src >= 0 && lane < 32)
-        lds_dma16((part ? g.a_lo : g.a) + size_t(src) * g.K + kb * KS + 8 * lane,
-                  lds_offset(ad + (part * 16 * MT + r) * ROWP * 2));
+      const int src = __builtin_amdgcn_readfirstlane(rows[r]);
+      if (src >= 0) asrc[j] = (part ? g.a_lo : g.a) + size_t(src) * g.K;
+      adst[j] = lds_offset(abuf + (part * 16 * MT + r) * ROWP * 2);
     }
-    uint8_t *sd = sbuf + half * Gm::SBUF;
-    for (int i = wave; i < NT; i += W) {  // rows 16 i .. 16 i + 15, four lanes (64 B) each
-      const int r = 16 * i + (lane >> 2), src = rows[r];
-      if (src >= 0)
-        lds_dma16(g.sums + (size_t(src) * nsteps + kb) * SUMS + 8 * (lane & 3), lds_offset(sd + (16 * i) * SUMS * 2));
-    }
+  }
+  const int srow = rows[16 * (wv < NT ? wv : 0) + (lane >> 2)];  // sums: rows 16 wave .. + 15, four lanes each
+  const uint16_t *ssrc = g.sums + size_t(srow < 0 ? 0 : srow) * nsteps * SUMS + 8 * (lane & 3);
+  auto issue = [&](int kb, int half) {
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+      if (asrc[j] != nullptr && lane < 32) lds_dma16_s(asrc[j] + kb * KS, 16 * lane, adst[j] + half * Gm::BUF);
+    if (wv < NT && srow >= 0)
+      lds_dma16(ssrc + kb * SUMS, lds_offset(sbuf + half * Gm::SBUF + (16 * wv) * SUMS * 2));
   };
   auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
 #pragma unroll
