@@ -8,6 +8,7 @@ from __future__ import annotations
 import concurrent.futures
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -35,12 +36,33 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _spills(report: str) -> list:
+    """Kernels of a -Rpass-analysis=kernel-resource-usage report that spill
+    registers or use scratch memory."""
+    bad, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"(SGPRs Spill|VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", line)
+        if m and int(m.group(2)) > 0:
+            bad.append(f"{name}: {m.group(1)} {m.group(2)}")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # every kernel keeps its state in registers: a spill is a build error (the
+    # hot loops are sized to fit, and the direct-to-LDS copy sequences are
+    # written for unspilled scalar state)
+    bad = _spills(r.stderr)
+    if bad:
+        raise RuntimeError(f"register spills in {os.path.basename(src)}:\n  " + "\n  ".join(bad))
     return obj
 
 

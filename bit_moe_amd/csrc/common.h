@@ -143,19 +143,6 @@ BM_DEVICE void lds_dma16(const void *p, uint32_t lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(base) : "memory");
 }
-// The same copy from a wave-uniform base (kept in an SGPR pair) plus a 32-bit
-// per-lane byte offset: no 64-bit address arithmetic in vector registers.
-BM_DEVICE void lds_dma16_s(const void *base, uint32_t voff, uint32_t lds) {
-  // readfirstlane returns int: both halves go through uint32_t so that the
-  // low word is zero-extended (a sign-extended low word would corrupt the
-  // high word of the address)
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
-  const uint64_t sb = (uint64_t(hi) << 32) | uint64_t(lo);
-  const uint32_t m = uint32_t(__builtin_amdgcn_readfirstlane(lds));
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "s"(m) : "memory");
-}
 // LDS byte offset of a generic pointer into shared memory
 BM_DEVICE uint32_t lds_offset(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));

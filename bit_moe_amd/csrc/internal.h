@@ -127,7 +127,14 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, hipStream_t stream);
 hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,
                                    hipStream_t stream);
-constexpr int PREFILL_BM = 48;       // tokens per chunk of the gate/up grouped GEMM (tile_off)
-constexpr int PREFILL_BM_DOWN = 32;  // pairs per chunk of the down grouped GEMM (tile_off2)
+// 16-row M-tiles per chunk of the routed grouped GEMMs
+#ifndef BM_PF_CHUNK_GU
+#define BM_PF_CHUNK_GU 3
+#endif
+#ifndef BM_PF_CHUNK_DN
+#define BM_PF_CHUNK_DN 2
+#endif
+constexpr int PREFILL_BM = 16 * BM_PF_CHUNK_GU;       // tokens per chunk of the gate/up grouped GEMM (tile_off)
+constexpr int PREFILL_BM_DOWN = 16 * BM_PF_CHUNK_DN;  // pairs per chunk of the down grouped GEMM (tile_off2)
 
 }  // namespace bm

@@ -33,8 +33,8 @@ namespace {
 constexpr int KS = 256;               // K per step (one super-block of every weight row)
 constexpr int ROWP = KS + 8;          // bf16 per LDS activation row (16-byte pad)
 constexpr int SUMS = 32;              // bf16 sums per (row, step): 16 sub-blocks x (hi, lo)
-constexpr int MT_GU = 3;              // gate/up: M-tiles of 16 per chunk (48 tokens)
-constexpr int MT_DN = 2;              // down: 32 pairs (its hi and lo rows double the LDS per row)
+constexpr int MT_GU = BM_PF_CHUNK_GU;  // gate/up: M-tiles of 16 per chunk
+constexpr int MT_DN = BM_PF_CHUNK_DN;  // down: M-tiles of 16 pairs per chunk (hi and lo rows: twice the LDS per row)
 
 }  // namespace
 
@@ -120,32 +120,24 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
   if constexpr (GATEUP) wb[1] = g.b1 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
   // copies of step kb into buffer half: activation rows (512 B each, half a
   // wave per row; this wave's rows wave, wave + W, ..) and their sums (64 B
-  // per row, 16 rows per instruction).  The row bases are wave-uniform and
-  // stay in scalar registers.
-  constexpr int NA = PARTS * 16 * NT, JA = (NA + W - 1) / W;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint16_t *asrc[JA];
-  uint32_t adst[JA];
-#pragma unroll
-  for (int j = 0; j < JA; ++j) {
-    const int i = wv + W * j;
-    asrc[j] = nullptr;
-    adst[j] = 0;
-    if (i < NA) {
-      const int part = i / (16 * NT), r = i % (16 * NT);
-      const int src = __builtin_amdgcn_readfirstlane(rows[r]);
-      if (src >= 0) asrc[j] = (part ? g.a_lo : g.a) + size_t(src) * g.K;
-      adst[j] = lds_offset(abuf + (part * 16 * MT + r) * ROWP * 2);
-    }
-  }
-  const int srow = rows[16 * (wv < NT ? wv : 0) + (lane >> 2)];  // sums: rows 16 wave .. + 15, four lanes each
-  const uint16_t *ssrc = g.sums + size_t(srow < 0 ? 0 : srow) * nsteps * SUMS + 8 * (lane & 3);
+  // per row, 16 rows per instruction).  Addresses are formed in vector
+  // registers: a variant with wave-uniform row bases in scalar registers
+  // gave wrong rows, run to run, in builds where those registers spilled.
   auto issue = [&](int kb, int half) {
-#pragma unroll
-    for (int j = 0; j < JA; ++j)
-      if (asrc[j] != nullptr && lane < 32) lds_dma16_s(asrc[j] + kb * KS, 16 * lane, adst[j] + half * Gm::BUF);
-    if (wv < NT && srow >= 0)
-      lds_dma16(ssrc + kb * SUMS, lds_offset(sbuf + half * Gm::SBUF + (16 * wv) * SUMS * 2));
+    uint8_t *ad = abuf + half * Gm::BUF;
+    for (int i = wave; i < PARTS * 16 * NT; i += W) {
+      const int part = i / (16 * NT), r = i % (16 * NT);
+      const int src = rows[r];
+      if (src >= 0 && lane < 32)
+        lds_dma16((part ? g.a_lo : g.a) + size_t(src) * g.K + kb * KS + 8 * lane,
+                  lds_offset(ad + (part * 16 * MT + r) * ROWP * 2));
+    }
+    uint8_t *sd = sbuf + half * Gm::SBUF;
+    for (int i = wave; i < NT; i += W) {  // rows 16 i .. 16 i + 15, four lanes (64 B) each
+      const int r = 16 * i + (lane >> 2), src = rows[r];
+      if (src >= 0)
+        lds_dma16(g.sums + (size_t(src) * nsteps + kb) * SUMS + 8 * (lane & 3), lds_offset(sd + (16 * i) * SUMS * 2));
+    }
   };
   auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
 #pragma unroll
@@ -302,8 +294,13 @@ __global__ void __launch_bounds__(64 * BM_GRP_WAVES) q2_group_kernel(GroupArgs g
     case 1: group_body<GATEUP, 1>(g, e, valid, base, ntile, smem_g, rows); break;
     case 2: group_body<GATEUP, 2>(g, e, valid, base, ntile, smem_g, rows); break;
     case 3: if constexpr (Gm::MT >= 3) group_body<GATEUP, 3>(g, e, valid, base, ntile, smem_g, rows); break;
-    default: if constexpr (Gm::MT >= 4) group_body<GATEUP, 4>(g, e, valid, base, ntile, smem_g, rows); break;
+    case 4: if constexpr (Gm::MT >= 4) group_body<GATEUP, 4>(g, e, valid, base, ntile, smem_g, rows); break;
+    case 5: if constexpr (Gm::MT >= 5) group_body<GATEUP, 5>(g, e, valid, base, ntile, smem_g, rows); break;
+    case 6: if constexpr (Gm::MT >= 6) group_body<GATEUP, 6>(g, e, valid, base, ntile, smem_g, rows); break;
+    case 7: if constexpr (Gm::MT >= 7) group_body<GATEUP, 7>(g, e, valid, base, ntile, smem_g, rows); break;
+    default: if constexpr (Gm::MT >= 8) group_body<GATEUP, 8>(g, e, valid, base, ntile, smem_g, rows); break;
   }
+  static_assert(Gm::MT >= 1 && Gm::MT <= 8, "chunks of 1 to 8 M-tiles");
 }
 
 size_t q2_group_smem(bool gateup) {

@@ -223,3 +223,19 @@ def test_residual_rescale_rejects_bad_args(lib):
     assert lib.bitmoe_residual_rescale(None, None, bm.BF16, 0, 4096, None, None) == bm.OK
     assert lib.bitmoe_residual_rescale(ctypes.c_void_p((1 << 20) + 4), fake, bm.F32, 4, 4096, fake, None) == bm.EINVAL
     assert lib.bitmoe_residual_rescale(fake, fake, bm.F32, -1, 4096, fake, None) == bm.EINVAL
+
+
+def test_build_rejects_spilling_kernels():
+    # the build parses the compiler's resource report and refuses spills
+    from bit_moe_amd import build as b
+    report = "\n".join([
+        "x.hip:1:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     SGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     VGPRs Spill: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark: Function Name: k_bad [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     SGPRs Spill: 30 [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    bad = b._spills(report)
+    assert bad == ["k_bad: SGPRs Spill 30", "k_bad: ScratchSize [bytes/lane] 12"]
