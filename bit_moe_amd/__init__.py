@@ -24,6 +24,7 @@ WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
 MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_DECODE_INT8 = 0, 1, 2, 3
 DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN, DEV_DUP_EXPERT = 1, 2, 4, 8
 LAYOUT_CANONICAL = 0
+NOALLOC_MAX_T = 8  # tokens per moe_route_noalloc call
 SCORE_SOFTMAX, SCORE_SQRT_SOFTPLUS = 0, 1
 FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
 
@@ -32,7 +33,7 @@ EXPORTS = [
     "bitmoe_plan_workspace_size", "moe_dequant", "moe_quantize_q8_1", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
-    "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size",
+    "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size", "moe_route_noalloc",
 ]
 
 
@@ -76,6 +77,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "bitmoe_workspace_size": [LP, I32, I32, ctypes.POINTER(SZ)],
         "moe_route": [LP, P, I32, I32, P, P, P, P, SZ, P],
+        "moe_route_noalloc": [LP, P, I32, I32, P, P, P, P],
         "moe_route_ex": [LP, P, I32, I32, ctypes.POINTER(_RouteOptsC), P, P, P, SZ, P],
         "moe_expert_ffn": [LP, P, I32, I32, P, P, P, I32, I32, P, SZ, P],
         "engram_gather": [P, I64, P, I64, P, P, P],
@@ -202,6 +204,27 @@ def route(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.
     lc = layer.c()
     _check(lib.moe_route(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids), _ptr(weights),
                          _ptr(ws), ws.numel(), _stream(stream)))
+    return ids, weights
+
+
+def route_noalloc(layer: Layer, x: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                  ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None, stream=None):
+    """moe_route_noalloc: moe_route with the library's per-device scratch in
+    place of a workspace (T <= NOALLOC_MAX_T)."""
+    lib = load()
+    _require(x, "x")
+    T = x.shape[0]
+    if ids is None:
+        ids = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    _require(ids, "ids", torch.int32)
+    _require(weights, "weights", torch.float32)
+    if bias is not None:
+        _require(bias, "bias", torch.float32)
+    lc = layer.c()
+    _check(lib.moe_route_noalloc(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids),
+                                 _ptr(weights), _stream(stream)))
     return ids, weights
 
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "bitmoe.h"
 #include "internal.h"
@@ -30,6 +31,44 @@ bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
 constexpr int MAX_DECODE_T = 8;
+
+// ---- per-device scratch of moe_route_noalloc ---------------------------------
+// The status record and the router logits of up to BITMOE_NOALLOC_MAX_T tokens
+// of up to 1024 experts, laid out as the common region of a workspace.
+constexpr size_t NOALLOC_SCRATCH_BYTES = 256 + size_t(BITMOE_NOALLOC_MAX_T) * 1024 * sizeof(float);
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+}  // namespace
+
+// One copy per device, held until the process ends.  In host code the name is
+// only a stand-in for the symbol: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+int scratch_address(const char *fn, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+    return fail(BITMOE_EUNSUPPORTED, "%s: device %d outside the %d devices with scratch slots", fn, dev,
+                NOALLOC_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(fn, e);
+    if (!ptr || !aligned(ptr, 256)) return fail(BITMOE_EHIP, "%s: scratch address %p unusable", fn, ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return BITMOE_OK;
+}
 
 int check_layer(const char *fn, const bitmoe_layer *L) {
   if (!L) return fail(BITMOE_EINVAL, "%s: layer is NULL", fn);
@@ -270,6 +309,37 @@ int moe_route(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, 
     return fail(BITMOE_EWORKSPACE, "%s: workspace has %zu bytes, needs %zu for T=%d", fn, ws_bytes, c.off, T);
   hipError_t e = bm::launch_route(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k, L->w_router,
                                   logit_bias, logits, topk_ids, topk_w, wsplit, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int moe_route_noalloc(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const float *logit_bias,
+                      int32_t *topk_ids, float *topk_w, hipStream_t stream) {
+  const char *fn = "moe_route_noalloc";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (T > BITMOE_NOALLOC_MAX_T)
+    return fail(BITMOE_EUNSUPPORTED, "%s: T=%d exceeds the scratch limit of %d tokens", fn, T, BITMOE_NOALLOC_MAX_T);
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (T == 0) return BITMOE_OK;
+  if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(BITMOE_EINVAL, "%s: topk_ids/topk_w NULL or misaligned", fn);
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(BITMOE_EINVAL, "%s: logit_bias misaligned", fn);
+  void *sc = nullptr;
+  if ((rc = scratch_address(fn, &sc))) return rc;
+  Carve c(sc);
+  int64_t *status;
+  float *logits;
+  uint16_t *wsplit;
+  carve_common(c, L, T, &status, &logits, &wsplit);  // no router split below MAX_DECODE_T tokens
+  if (c.off > NOALLOC_SCRATCH_BYTES || wsplit)
+    return fail(BITMOE_EUNSUPPORTED, "%s: needs %zu bytes of scratch, has %zu", fn, c.off, NOALLOC_SCRATCH_BYTES);
+  // the logits are written in full before they are read: nothing in the
+  // scratch has to start at zero
+  hipError_t e = bm::launch_route(x, x_dtype == BITMOE_BF16, T, L->d_model, L->n_experts, L->top_k, L->w_router,
+                                  logit_bias, logits, topk_ids, topk_w, nullptr, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }
