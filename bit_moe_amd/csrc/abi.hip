@@ -129,6 +129,7 @@ struct PrefillWs {
   bm::PlanBufs plan;
   int32_t *tile_off, *tile_off2;
   uint16_t *xs, *h, *hs, *h_lo, *hs_lo, *sw, *xsum;
+  float *xtot;
   float *y, *ys;
 };
 
@@ -227,6 +228,8 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   w->ys = static_cast<float *>(c.take(size_t(T) * L->d_model * 4));
   // sub-block sums of the grouped GEMMs' activation rows: 32 bf16 per row and 256 columns
   w->xsum = static_cast<uint16_t *>(c.take(std::max(size_t(T) * L->d_model, P * L->d_ff) / 256 * 32 * 2));
+  // their float32 super-block sums: one per row and 256 columns
+  w->xtot = static_cast<float *>(c.take(std::max(size_t(T) * L->d_model, P * L->d_ff) / 256 * 4));
 }
 
 size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
@@ -448,6 +451,7 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   a.hs_lo = w.hs_lo;
   a.sw_bf16 = w.sw;
   a.xsum = w.xsum;
+  a.xtot = w.xtot;
   a.y = w.y;
   a.ys = w.ys;
   a.out = y;

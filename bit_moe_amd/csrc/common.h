@@ -143,6 +143,11 @@ BM_DEVICE void lds_dma16(const void *p, uint32_t lds) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(base) : "memory");
 }
+// 4-byte variant: lane l's dword lands at LDS byte lds + 4 l.
+BM_DEVICE void lds_dma4(const void *p, uint32_t lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(p), "s"(base) : "memory");
+}
 // LDS byte offset of a generic pointer into shared memory
 BM_DEVICE uint32_t lds_offset(const void *p) {
   return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));

@@ -115,6 +115,7 @@ struct PrefillArgs {
   uint16_t *hs_lo;
   uint16_t *sw_bf16;   // [3][F*D] bf16 copy of the shared expert (gate, up, down)
   uint16_t *xsum;      // activation sub-block sums of the grouped GEMMs: max(T*D, T*k*F) / 8 bf16
+  float *xtot;         // activation super-block sums (float32): max(T*D, T*k*F) / 256
   float *y;            // [T*k][D] float32, pair order
   float *ys;           // [T][D]
   void *out;
@@ -124,7 +125,8 @@ struct PrefillArgs {
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
 // routed grouped GEMM (gate/up with h out, or down with y out) over the plan's
 // chunks, after the activation rows' sub-block sums (into sums)
-hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, hipStream_t stream);
+hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, float *tot,
+                           hipStream_t stream);
 hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,
                                    hipStream_t stream);
 // 16-row M-tiles per chunk of the routed grouped GEMMs

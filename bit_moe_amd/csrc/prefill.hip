@@ -209,8 +209,8 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
   const size_t q2_stride = size_t(a.F) * a.D / 256 * 84;
 
   // routed gate/up (A = x rows by token, N = F), then down (A = h hi + lo rows by pair, N = D)
-  if ((err = launch_q2_group(true, a, x, a.xsum, stream)) != hipSuccess) return err;
-  if ((err = launch_q2_group(false, a, x, a.xsum, stream)) != hipSuccess) return err;
+  if ((err = launch_q2_group(true, a, x, a.xsum, a.xtot, stream)) != hipSuccess) return err;
+  if ((err = launch_q2_group(false, a, x, a.xsum, a.xtot, stream)) != hipSuccess) return err;
 
   if (a.sg) {
     // shared expert: expand Q8_0 to exact bf16 codes + float scales, then dense GEMMs

@@ -5,7 +5,11 @@
 // routed experts as grouped expert matrix products.  Here on
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation and exact weights (the
 // offset form of mfma_q2.h: B = 128 + sc*q per weight, the sub-block sums of
-// the activations against B = m and B = -128, d and dmin on the float32 sums).
+// the activations against B = m, d and dmin on the float32 sums).  The main
+// accumulators start from -128 times the row's float32 super-block sum (the
+// same for every output column, so no MFMA is needed for it): the sum is
+// exact for bf16 data of ordinary range, where a bf16 hi + lo split of it
+// would leave 2^-17 of it, times 128, in every output.
 //
 // The operand build (code unpack and table lookup, ~11 VALU instructions per
 // 8 weights and lane) is the costly part, so a block owns one chunk of an
@@ -41,11 +45,15 @@ constexpr int MT_DN = BM_PF_CHUNK_DN;  // down: M-tiles of 16 pairs per chunk (h
 // ---- activation sub-block sums --------------------------------------------
 // out[row][kb][slot]: the 16 sub-block sums of columns [256 kb, 256 kb + 256)
 // of row `row` (over both parts when a_lo is given), each split into bf16 hi +
-// lo and placed at q2_sum_slot(sub-block, part).  One thread per sub-block.
+// lo and placed at q2_sum_slot(sub-block, part); tot[row][kb]: their float32
+// total.  One thread per sub-block; the 16 threads of a super-block are 16
+// consecutive lanes of one wave.
 __global__ void __launch_bounds__(256) xsum_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict__ a_lo,
-                                                   int64_t rows, int K, uint16_t *__restrict__ out) {
+                                                   int64_t rows, int K, uint16_t *__restrict__ out,
+                                                   float *__restrict__ tot) {
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;  // (row, sub-block of the row)
   const int nsb = K / 16;
+  // rows * nsb is a multiple of 16: a super-block's 16 lanes are all in range or all out
   if (i >= rows * nsb) return;
   const int64_t row = i / nsb;
   const int c = int(i % nsb), kb = c >> 4, sb = c & 15;
@@ -61,6 +69,10 @@ __global__ void __launch_bounds__(256) xsum_kernel(const uint16_t *__restrict__ 
   uint16_t *o = out + (row * (K / KS) + kb) * SUMS;
   o[q2_sum_slot(sb, 0)] = shi;
   o[q2_sum_slot(sb, 1)] = f32_to_bf16(sum - bf16_to_f32(shi));
+  float t = sum;
+#pragma unroll
+  for (int m = 8; m > 0; m >>= 1) t += __shfl_xor(t, m, 16);
+  if (sb == 0) tot[row * (K / KS) + kb] = t;
 }
 
 // ---- grouped GEMM ---------------------------------------------------------------
@@ -72,6 +84,7 @@ struct GroupArgs {
   const uint16_t *a, *a_lo;                           // activation rows (a_lo: down's lo parts)
   int a_by_pair;                                      // row index = pair (down) or token (gate/up)
   const uint16_t *sums;                               // xsum_kernel output for the same rows
+  const float *tot;                                   // and their super-block totals
   const uint8_t *b0, *b1;                             // Q2 matrices [E][N][K/256] (b1: up)
   size_t b_stride;                                    // bytes per expert matrix
   uint16_t *h, *h_lo;                                 // gate/up out [pairs][N]
@@ -101,6 +114,9 @@ struct GroupGeo {
   static constexpr int BN = 16 * NG * WAVES;                       // weight rows per block
   static constexpr int BUF = PARTS * 16 * MT * ROWP * 2;  // bytes of one activation buffer
   static constexpr int SBUF = 16 * MT * SUMS * 2;         // bytes of one sums buffer
+  static constexpr int TBUF = 16 * MT * 4;                // bytes of one buffer of super-block totals
+  static constexpr int ROWS_OFF = 2 * BUF + 2 * SBUF + 2 * TBUF;  // chunk row table
+  static constexpr size_t SMEM = size_t(ROWS_OFF) + 16 * MT * 4;
 };
 
 template <bool GATEUP, int NT>
@@ -109,6 +125,7 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
   constexpr int NM = Gm::NM, PARTS = Gm::PARTS, MT = Gm::MT, NG = Gm::NG;
   uint8_t *abuf = smem;
   uint8_t *sbuf = smem + 2 * Gm::BUF;
+  uint8_t *tbuf = sbuf + 2 * Gm::SBUF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, nl = lane & 15, p = gq & 1;
   const int nsteps = g.K / KS;
@@ -138,6 +155,10 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
       if (src >= 0)
         lds_dma16(g.sums + (size_t(src) * nsteps + kb) * SUMS + 8 * (lane & 3), lds_offset(sd + (16 * i) * SUMS * 2));
     }
+    if (wave == W - 1 && lane < 16 * NT) {  // totals: one dword per row
+      const int src = rows[lane];
+      if (src >= 0) lds_dma4(g.tot + size_t(src) * nsteps + kb, lds_offset(tbuf + half * Gm::TBUF));
+    }
   };
   auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
 #pragma unroll
@@ -162,7 +183,6 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
 #pragma unroll
     for (int m = 0; m < NM; ++m) q2_settle(cur[ng][m]);
   __syncthreads();
-  const uint32_t Bm128[4] = {0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
   for (int kb = 0; kb < nsteps; ++kb) {
     const int half = kb & 1;
     Q2Raw nxt[NG][NM];
@@ -172,14 +192,17 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
     }
     const uint16_t *Ah = reinterpret_cast<const uint16_t *>(abuf + half * Gm::BUF);
     const uint16_t *Sx = reinterpret_cast<const uint16_t *>(sbuf + half * Gm::SBUF);
-    // the main accumulators start from -128 x the rows' super-block sums,
-    // which removes the 128 offset of the main operands
+    const float *Xt = reinterpret_cast<const float *>(tbuf + half * Gm::TBUF);
+    // the main accumulators start from -128 x the rows' super-block sums
+    // (rows 4 gq .. 4 gq + 3 of the tile in this lane), which removes the 128
+    // offset of the main operands
     uint32_t As[NT][4];
     f32x4_t cm[NT][NG][NM];
 #pragma unroll
     for (int mi = 0; mi < NT; ++mi) {
       ld16(Sx + (16 * mi + nl) * SUMS + 8 * gq, As[mi]);
-      const f32x4_t cx = mfma16(As[mi], Bm128, zero);
+      const float4 xt = *reinterpret_cast<const float4 *>(Xt + 16 * mi + 4 * gq);
+      const f32x4_t cx = {-128.f * xt.x, -128.f * xt.y, -128.f * xt.z, -128.f * xt.w};
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
@@ -263,10 +286,11 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
 }
 
 template <bool GATEUP>
-__global__ void __launch_bounds__(64 * BM_GRP_WAVES) q2_group_kernel(GroupArgs g) {
+__global__ void __launch_bounds__(64 * BM_GRP_WAVES) __attribute__((amdgpu_waves_per_eu(GATEUP ? 2 : 4)))
+q2_group_kernel(GroupArgs g) {
   using Gm = GroupGeo<GATEUP>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem_g[];
-  int32_t *rows = reinterpret_cast<int32_t *>(smem_g + 2 * Gm::BUF + 2 * Gm::SBUF);  // activation row, -1: padding
+  int32_t *rows = reinterpret_cast<int32_t *>(smem_g + Gm::ROWS_OFF);  // activation row, -1: padding
   const int nt_n = g.N / Gm::BN;
   const int G = gridDim.x, b = blockIdx.x;
   const int L = (b & 7) * (G >> 3) + (b >> 3);  // XCD-aware: each XCD takes a contiguous range
@@ -303,17 +327,16 @@ __global__ void __launch_bounds__(64 * BM_GRP_WAVES) q2_group_kernel(GroupArgs g
   static_assert(Gm::MT >= 1 && Gm::MT <= 8, "chunks of 1 to 8 M-tiles");
 }
 
-size_t q2_group_smem(bool gateup) {
-  if (gateup) return size_t(2) * GroupGeo<true>::BUF + 2 * GroupGeo<true>::SBUF + 16 * MT_GU * 4;
-  return size_t(2) * GroupGeo<false>::BUF + 2 * GroupGeo<false>::SBUF + 16 * MT_DN * 4;
-}
+size_t q2_group_smem(bool gateup) { return gateup ? GroupGeo<true>::SMEM : GroupGeo<false>::SMEM; }
 
 // Routed gate/up (gateup) or down over the plan's chunks of 48 tokens
 // (tile_off) or 32 pairs (tile_off2) per expert, 256 weight rows per block.
-// sums: workspace for the activations' sub-block sums (K / 4 bytes per row:
-// tokens for gate/up, pairs for down).  hipErrorNotSupported when N is not a
-// multiple of the block's rows (nothing is launched then).
-hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, hipStream_t stream) {
+// sums, tot: workspace for the activations' sub-block sums (K / 4 bytes per
+// row) and super-block totals (K / 64 bytes per row), rows being tokens for
+// gate/up and pairs for down.  hipErrorNotSupported when N is not a multiple
+// of the block's rows (nothing is launched then).
+hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, float *tot,
+                           hipStream_t stream) {
   GroupArgs g{};
   g.E = a.E;
   g.k = a.k;
@@ -326,6 +349,7 @@ hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x,
   const int P = a.T * a.k;
   g.n_chunks = (P + 16 * mt - 1) / (16 * mt) + min(a.E, P);
   g.sums = sums;
+  g.tot = tot;
   const int bn = gateup ? GroupGeo<true>::BN : GroupGeo<false>::BN;
   if (gateup) {
     g.K = a.D, g.N = a.F;
@@ -344,7 +368,7 @@ hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x,
   const int64_t rows = gateup ? a.T : P;
   const int64_t nthreads = rows * (g.K / 16);
   BM_LAUNCH("xsum_kernel", xsum_kernel, dim3(unsigned((nthreads + 255) / 256)), dim3(256), 0, stream, g.a, g.a_lo,
-            rows, g.K, sums);
+            rows, g.K, sums, tot);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t smem = q2_group_smem(gateup);

@@ -126,6 +126,9 @@ def test_inject_large_batch_sampled_tokens():
     _compare(got[idx], g[idx], want, gw, rows[idx], w, res[idx])
     for t in (3, 700):
         assert np.array_equal(got[t], res[t]) and g[t].tolist() == [0.0] * 4
+    # run twice: the same inputs give the same bits (residual and gates)
+    got2, g2 = _run(rows, w, qn, kn, 1e-6, res, mask)
+    assert np.array_equal(got2, got) and np.array_equal(g2.view(np.uint32), g.view(np.uint32))
 
 
 def test_inject_every_position_masked():

@@ -108,3 +108,41 @@ def test_stack_sampled_layers(stack, T):
     for l, (out, key, j) in rows.items():
         ref = engram.gather(lambda r, k=key: synthdata.engram_rows(k, r), synthdata.ENGRAM_ROWS, rid[:, j, :])
         assert compare.bf16_bits_equal(_bits(out), ref), l
+
+
+def test_stack_prefill_sampled_layers(stack):
+    """The 40 layers over a prefill chunk of T = 8192 tokens (grouped-GEMM
+    path), layer-local checks of sampled tokens at the sampled layers."""
+    cfg, lds, layers, tables = stack
+    T = cfg.prefill_T
+    x = torch.from_numpy(synthdata.activations_bf16(1, 90, T, cfg.d_model).view(np.int16)).cuda()
+    x = x.view(torch.bfloat16)
+    ws = bm.workspace(layers[0], T, bm.MODE_PREFILL)
+    saved = {}
+    for l in range(cfg.n_layers):
+        ids, w = bm.route(layers[l], x, ws)
+        y = bm.expert_ffn(layers[l], x, ids, w, ws, mode=bm.MODE_PREFILL)
+        xn = bm.residual_rescale(x, y)
+        if l in SAMPLED:
+            saved[l] = (x.clone(), ids.clone(), y.clone(), xn.clone())
+        x = xn
+    torch.cuda.synchronize()
+    code, _ = bm.read_status(bm.ws_status(ws))
+    assert code == 0
+    print(f"[stack] prefill T={T}: {cfg.n_layers} layers run", flush=True)
+    rng = np.random.default_rng(8)
+    for l in SAMPLED:
+        xin, ids, y, xn = saved[l]
+        # first and last token of the chunk and two more
+        sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=2, replace=False)]))
+        xv = formats.bf16_to_f64(_bits(xin)[sample])
+        ids_h = ids.cpu().numpy()[sample]
+        r_ids, _, L = moe.route(xv, lds[l].router(), cfg.top_k)
+        _, _, bad = compare.compare_ids(ids_h, r_ids, L)
+        assert not bad, (l, bad)
+        ref = moe.moe_layer(oracle_layer(lds[l]), xv, ids=ids_h)
+        yv = formats.bf16_to_f64(_bits(y)[sample])
+        err = compare.max_rel_error(yv, ref.out)
+        print(f"[parity] stack prefill layer {l} tokens {sample.tolist()} max rel err {err:.3e}", flush=True)
+        assert err < TOL
+        assert np.array_equal(_bits(xn)[sample], moe.residual_rescale(xv, yv))
