@@ -338,9 +338,12 @@ def bench_int8_decode(bm, torch, np, synthdata, args, lut, dev) -> dict:
     return out
 
 
-def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
-    """Prefill chunk T=4096 through one layer with the Zipf router bias."""
-    cfg = synthdata.CONFIGS["prefill"]
+def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
+    """Prefill chunk T=4096 through one layer with the Zipf router bias (lambda
+    = lam, else --zipf-lambda)."""
+    import dataclasses
+    lam = args.zipf_lambda if lam is None else lam
+    cfg = dataclasses.replace(synthdata.CONFIGS["prefill"], zipf_lambda=lam)
     L, ld = make_layer(bm, torch, synthdata, cfg, args.seed, 0, lut, dev)
     T, k, D, F = cfg.T, cfg.top_k, cfg.d_model, cfg.d_ff
     K, W = args.prefill_steps, 2
@@ -366,11 +369,12 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev) -> dict:
     gemm_ms = sum(prof.get(n, (0.0, 1))[0] for n in gemm_flops) / K
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.n_experts)
     return {"workload": "prefill chunk T=4096 through one layer (384 experts top-6, Zipf(1.1) router bias "
-                        "lambda=0.3, Q8_0 shared expert)",
+                        f"lambda={lam}, Q8_0 shared expert)",
             "tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 4),
             "tflops_step": round((routed + shared) / (step_ms * 1e-3) / 1e12, 1),
             "tflops_grouped_gemm": round((routed + shared) / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
             "mfma_bf16_peak_tflops": 2500.0,
+            "mfma_bf16_measured_tflops": args.measured.get("mfma_bf16_tflops") if hasattr(args, "measured") else None,
             "expert_tokens": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
             "kernels": kernel_table(prof, {}, gemm_flops)}
 
@@ -552,6 +556,40 @@ def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
     return out
 
 
+def measure_peaks(bm, torch, dev) -> dict:
+    """Achievable HBM read bandwidth (bitmoe_probe_read over 2 GiB) and dense
+    bf16 MFMA rate (bitmoe_probe_mfma), best of 5 event-timed runs each."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    n = 2 << 30
+    buf = torch.ones(n, dtype=torch.uint8, device=dev)
+    best_read = 0.0
+    for blocks in (2048, 8192):
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bm.probe_read(buf, n, sink, blocks)
+            e1.record()
+            e1.synchronize()
+            best_read = max(best_read, n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    blocks, iters = 2048, 2000
+    flops = blocks * 4 * iters * 4 * 32768.0
+    best_mfma = 0.0
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bm.probe_mfma(blocks, iters, sink)
+        e1.record()
+        e1.synchronize()
+        best_mfma = max(best_mfma, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbps": round(best_read, 1), "hbm_peak_gbps": HBM_PEAK_GBPS,
+            "mfma_bf16_tflops": round(best_mfma, 1), "mfma_bf16_peak_tflops": 2500.0,
+            "how": "best of 5 event-timed runs: a 2 GiB streaming read (16-byte loads, 4 in flight per lane, "
+                   "2048 and 8192 blocks) and 8192 waves x 2000 rounds of 4 independent 32x32x16 bf16 MFMAs "
+                   "on registers"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -571,6 +609,8 @@ def main() -> int:
                     choices=["verify", "int8_decode", "prefill", "router_variants", "engram_inject", "stack"],
                     help="run only these of the workloads beside the decode line")
     ap.add_argument("--stack-prefill-steps", type=int, default=2)
+    ap.add_argument("--zipf-lambda", type=float, default=0.3,
+                    help="strength of the Zipf(1.1) router bias of the prefill line (a lambda=1 line runs beside it)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run 3 plain device-to-device copies of MIB MiB (reference kernel for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -601,6 +641,9 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 3 x {args.copy_calibration} MiB device-to-device copies")
         del src, dst
+    args.measured = measure_peaks(bm, torch, dev)
+    log(f"[bench] measured peaks: {args.measured['hbm_read_gbps']} GB/s read, "
+        f"{args.measured['mfma_bf16_tflops']} TFLOP/s bf16 MFMA")
     cfg = synthdata.CONFIGS["decode"]
     K, W, NI = args.steps, args.warmup, args.instances
     lut = torch.from_numpy(synthdata.half_normal_lut().view(np.int16).copy()).to(dev)
@@ -657,7 +700,10 @@ def main() -> int:
                                "2-bit super-block experts, Q8_0 shared expert, bf16 activations",
                    "layer_instances": NI, "timing": "hip graph replay" if graph_ms is not None else "eager"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "measured_peak": args.measured["hbm_read_gbps"],
+                     "frac_of_measured": round(achieved / args.measured["hbm_read_gbps"], 4)},
+        "measured_peaks": args.measured,
         "hbm_gbps_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
         "eager_ms_per_step": round(eager_ms / K, 5),
         "kernels": kernel_table(prof, alg),
@@ -670,6 +716,10 @@ def main() -> int:
         log(f"[bench] {name} workload")
         out[name] = fn(bm, torch, np, synthdata, args, lut, dev)
         torch.cuda.empty_cache()
+        if name == "prefill" and args.zipf_lambda != 1.0:
+            log("[bench] prefill workload, lambda=1")
+            out["prefill_lambda1"] = fn(bm, torch, np, synthdata, args, lut, dev, lam=1.0)
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens, args.cpu_repeats)

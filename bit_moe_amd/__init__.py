@@ -34,6 +34,7 @@ EXPORTS = [
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
     "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size", "moe_route_noalloc",
+    "bitmoe_probe_mfma",
 ]
 
 
@@ -88,6 +89,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "bitmoe_fill": [P, I64, ctypes.c_uint64, I32, P, P],
         "bitmoe_read_status": [P, P, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "bitmoe_probe_read": [P, I64, P, I32, P],
+        "bitmoe_probe_mfma": [I32, I32, P, P],
         "bitmoe_residual_rescale": [P, P, I32, I32, I32, P, P],
         "engram_inject_workspace_size": [I32, I32, ctypes.POINTER(SZ)],
         "engram_inject": [P, I32, I32, P, I32, P, P, ctypes.c_float, P, P, P, P, SZ, P],
@@ -412,6 +414,11 @@ def profile_stop() -> dict:
 def probe_read(src: torch.Tensor, n_bytes: int, sink: torch.Tensor, blocks: int, stream=None) -> None:
     """Enqueue the streaming-read probe over the first n_bytes of src."""
     _check(load().bitmoe_probe_read(_ptr(src), n_bytes, _ptr(sink), blocks, _stream(stream)))
+
+
+def probe_mfma(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue the matrix-core probe: blocks x 4 waves x iters x 4 bf16 32x32x16 MFMAs (32,768 flops each)."""
+    _check(load().bitmoe_probe_mfma(blocks, iters, _ptr(sink), _stream(stream)))
 
 
 def residual_rescale(x: torch.Tensor, y: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -590,6 +590,14 @@ int bitmoe_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, int32_t 
   return BITMOE_OK;
 }
 
+int bitmoe_probe_mfma(int32_t blocks, int32_t iters, uint32_t *sink, hipStream_t stream) {
+  if (!sink || !aligned(sink, 4) || blocks < 1 || blocks > (1 << 20) || iters < 0)
+    return fail(BITMOE_EINVAL, "bitmoe_probe_mfma: bad arguments (blocks=%d iters=%d)", blocks, iters);
+  hipError_t e = bm::launch_probe_mfma(blocks, iters, sink, stream);
+  if (e != hipSuccess) return hip_fail("bitmoe_probe_mfma", e);
+  return BITMOE_OK;
+}
+
 int bitmoe_residual_rescale(const void *x, const void *y, int32_t y_dtype, int32_t T, int32_t D, void *x_out,
                             hipStream_t stream) {
   const char *fn = "bitmoe_residual_rescale";

@@ -125,6 +125,7 @@ struct PrefillArgs {
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
 // routed grouped GEMM (gate/up with h out, or down with y out) over the plan's
 // chunks, after the activation rows' sub-block sums (into sums)
+hipError_t launch_probe_mfma(int blocks, int iters, uint32_t *sink, hipStream_t stream);
 hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, float *tot,
                            hipStream_t stream);
 hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,

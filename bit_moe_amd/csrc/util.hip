@@ -161,4 +161,41 @@ hipError_t launch_probe_read(const void *src, int64_t n_bytes, uint32_t *sink, i
   return hipGetLastError();
 }
 
+// ---- matrix-core probe (achievable bf16 MFMA rate) -------------------------
+// Every wave runs `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16
+// accumulations on register operands (no memory traffic; 32,768 flops each)
+// and folds the accumulators into one word so the work cannot be dropped.
+// (The 16x16x32 shape needs about 16 independent accumulators per wave to
+// reach the same rate: a dependent one waits for its predecessor.)
+__global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, uint32_t *__restrict__ sink) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+  const uint32_t lane = threadIdx.x & 63;
+  // small finite bf16 operands that differ per lane (1 + lane/128 and 2^-12)
+  const uint32_t a1 = 0x3F80u + (lane & 0x7Fu) / 2u, b1 = 0x3980u;
+  const v4u av = {a1 | (a1 << 16), a1 | (a1 << 16), a1 | (a1 << 16), a1 | (a1 << 16)};
+  const v4u bv = {b1 | (b1 << 16), b1 | (b1 << 16), b1 | (b1 << 16), b1 | (b1 << 16)};
+  const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av), b = __builtin_bit_cast(bf16x8_t, bv);
+  f32x16_t c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) c[j][q] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += c[j][q];
+  if (__float_as_uint(s) == 0x9E3779B9u) sink[0] = __float_as_uint(s);  // practically never taken
+}
+
+hipError_t launch_probe_mfma(int blocks, int iters, uint32_t *sink, hipStream_t stream) {
+  BM_LAUNCH("probe_mfma_kernel", probe_mfma_kernel, dim3(blocks), dim3(256), 0, stream, iters, sink);
+  return hipGetLastError();
+}
+
 }  // namespace bm
