@@ -64,6 +64,7 @@ def test_workspace_size_valid_layer(lib):
 
 @pytest.mark.parametrize("field,value,code", [
     ("d_model", 300, bm.EUNSUPPORTED), ("d_model", 8192, bm.EUNSUPPORTED), ("d_ff", 96, bm.EUNSUPPORTED),
+    ("d_model", 3072, bm.EUNSUPPORTED), ("d_ff", 1536, bm.EUNSUPPORTED),  # multiples of 256, not powers of two
     ("n_experts", 0, bm.EUNSUPPORTED), ("n_experts", 2000, bm.EUNSUPPORTED), ("top_k", 0, bm.EINVAL),
     ("top_k", 9, bm.EINVAL), ("wfmt", 7, bm.EUNSUPPORTED), ("shared_wfmt", 5, bm.EUNSUPPORTED),
     ("w_gate", 0, bm.EINVAL), ("w_up", 0x10004, bm.EINVAL), ("w_router", 0, bm.EINVAL), ("ws_down", 0, bm.EINVAL),
