@@ -338,9 +338,10 @@ def bench_int8_decode(bm, torch, np, synthdata, args, lut, dev) -> dict:
     return out
 
 
-def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
+def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None, mode=None) -> dict:
     """Prefill chunk T=4096 through one layer with the Zipf router bias (lambda
-    = lam, else --zipf-lambda)."""
+    = lam, else --zipf-lambda), in the bf16 path or (mode) the int8 numerics."""
+    mode = bm.MODE_PREFILL if mode is None else mode
     import dataclasses
     lam = args.zipf_lambda if lam is None else lam
     cfg = dataclasses.replace(synthdata.CONFIGS["prefill"], zipf_lambda=lam)
@@ -349,7 +350,7 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
     K, W = args.prefill_steps, 2
     xs = [torch.from_numpy(ld.x(tag).view(np.int16)).to(dev).view(torch.bfloat16) for tag in range(2)]
     bias = torch.from_numpy(ld.bias()).to(dev)
-    ws = bm.workspace(L, T, bm.MODE_PREFILL)
+    ws = bm.workspace(L, T, mode)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
     y = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
@@ -357,7 +358,7 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
     def step(i):
         x = xs[i % 2]
         bm.route(L, x, ws, bias=bias, ids=ids, weights=wts)
-        bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=bm.MODE_PREFILL)
+        bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=mode)
 
     graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, False)
     step_ms = eager_ms / K
@@ -366,6 +367,9 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
     # useful FLOP per launch of each expert GEMM
     gemm_flops = {"routed_gateup_gemm_kernel": 2.0 * T * k * 2 * D * F, "routed_down_gemm_kernel": 2.0 * T * k * D * F,
                   "shared_gateup_gemm_kernel": 2.0 * T * 2 * D * F, "shared_down_gemm_kernel": 2.0 * T * D * F}
+    if mode == bm.MODE_PREFILL_INT8:  # the same products as int8 MACs (2 ops each)
+        gemm_flops = {n.replace("routed_", "routed_i8_").replace("shared_", "shared_i8_"): v
+                      for n, v in gemm_flops.items()}
     gemm_ms = sum(prof.get(n, (0.0, 1))[0] for n in gemm_flops) / K
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=cfg.n_experts)
     return {"workload": "prefill chunk T=4096 through one layer (384 experts top-6, Zipf(1.1) router bias "
@@ -373,6 +377,8 @@ def bench_prefill(bm, torch, np, synthdata, args, lut, dev, lam=None) -> dict:
             "tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 4),
             "tflops_step": round((routed + shared) / (step_ms * 1e-3) / 1e12, 1),
             "tflops_grouped_gemm": round((routed + shared) / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+            "numerics": "int8 activations (q8_1 blocks), int8 MFMA" if mode == bm.MODE_PREFILL_INT8 else "bf16",
+            "mfma_peak_tflops": 5000.0 if mode == bm.MODE_PREFILL_INT8 else 2500.0,
             "mfma_bf16_peak_tflops": 2500.0,
             "mfma_bf16_measured_tflops": args.measured.get("mfma_bf16_tflops") if hasattr(args, "measured") else None,
             "expert_tokens": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
@@ -719,6 +725,10 @@ def main() -> int:
         if name == "prefill" and args.zipf_lambda != 1.0:
             log("[bench] prefill workload, lambda=1")
             out["prefill_lambda1"] = fn(bm, torch, np, synthdata, args, lut, dev, lam=1.0)
+            torch.cuda.empty_cache()
+        if name == "prefill":
+            log("[bench] prefill workload, int8 numerics")
+            out["prefill_int8"] = fn(bm, torch, np, synthdata, args, lut, dev, mode=bm.MODE_PREFILL_INT8)
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libbitmoe.so")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 WFMT_NONE, WFMT_Q2SB, WFMT_Q8_0 = 0, 1, 2
-MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_DECODE_INT8 = 0, 1, 2, 3
+MODE_AUTO, MODE_DECODE, MODE_PREFILL, MODE_DECODE_INT8, MODE_PREFILL_INT8 = 0, 1, 2, 3, 4
 DEV_BAD_EXPERT, DEV_BAD_ROW, DEV_BAD_TOKEN, DEV_DUP_EXPERT = 1, 2, 4, 8
 LAYOUT_CANONICAL = 0
 NOALLOC_MAX_T = 8  # tokens per moe_route_noalloc call

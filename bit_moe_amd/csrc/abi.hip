@@ -232,6 +232,40 @@ void carve_prefill(Carve &c, const bitmoe_layer *L, int T, PrefillWs *w) {
   w->xtot = static_cast<float *>(c.take(std::max(size_t(T) * L->d_model, P * L->d_ff) / 256 * 4));
 }
 
+// int8 numerics on the prefill path: plan, quantised x and h with their
+// scales and stored sums, h in float32, the shared expert's int8 codes
+void carve_prefill_i8(Carve &c, const bitmoe_layer *L, int T, bm::PrefillI8Args *a) {
+  const int E = L->n_experts, D = L->d_model, F = L->d_ff;
+  const size_t P = size_t(T) * L->top_k;
+  a->plan.counts = static_cast<int32_t *>(c.take(size_t(E) * 4));
+  a->plan.offsets = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  a->plan.perm = static_cast<int32_t *>(c.take(P * 4));
+  a->plan.union_ids = static_cast<int32_t *>(c.take(size_t(E) * 4));
+  a->plan.n_union = static_cast<int32_t *>(c.take(4));
+  a->plan.chunk_counts = static_cast<int32_t *>(c.take(bm::plan_scratch_bytes(T, E)));
+  a->tile_off = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  a->tile_off2 = static_cast<int32_t *>(c.take(size_t(E + 1) * 4));
+  a->plan.tile_off = a->tile_off;
+  a->plan.tile_off2 = a->tile_off2;
+  a->xq = static_cast<int8_t *>(c.take(size_t(T) * D));
+  a->xd = static_cast<float *>(c.take(size_t(T) * D / 32 * 4));
+  a->xs = static_cast<float *>(c.take(size_t(T) * D / 16 * 4));
+  a->sums = static_cast<uint16_t *>(c.take(std::max(size_t(T) * D, P * F) / 256 * 32 * 2));
+  a->hf = static_cast<float *>(c.take(P * F * 4));
+  a->hq = static_cast<int8_t *>(c.take(P * F));
+  a->hd = static_cast<float *>(c.take(P * F / 32 * 4));
+  a->hs = static_cast<float *>(c.take(P * F / 16 * 4));
+  const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
+  a->sw_i8 = static_cast<int8_t *>(c.take(shared ? size_t(3) * F * D : 0));
+  a->sw_d = static_cast<float *>(c.take(shared ? size_t(3) * F * D / 32 * 4 : 0));
+  a->hsf = static_cast<float *>(c.take(size_t(T) * F * 4));
+  a->hsq = static_cast<int8_t *>(c.take(size_t(T) * F));
+  a->hsd = static_cast<float *>(c.take(size_t(T) * F / 32 * 4));
+  a->hss = static_cast<float *>(c.take(size_t(T) * F / 16 * 4));
+  a->y = static_cast<float *>(c.take(P * D * 4));
+  a->ys = static_cast<float *>(c.take(size_t(T) * D * 4));
+}
+
 size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
   Carve c(nullptr);
   carve_common(c, L, T, nullptr, nullptr);
@@ -243,6 +277,9 @@ size_t ws_bytes_for(const bitmoe_layer *L, int T, int mode) {
     DecodeWs w;
     float *hf, *hsf;
     carve_decode_i8(c, L, T, &w, &hf, &hsf);
+  } else if (m == BITMOE_MODE_PREFILL_INT8) {
+    bm::PrefillI8Args a{};
+    carve_prefill_i8(c, L, T, &a);
   } else {
     PrefillWs w;
     carve_prefill(c, L, T, &w);
@@ -281,7 +318,7 @@ int bitmoe_workspace_size(const bitmoe_layer *L, int32_t T, int32_t mode, size_t
   if (rc) return rc;
   if (!bytes) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: bytes is NULL");
   if (T < 0) return fail(BITMOE_EINVAL, "bitmoe_workspace_size: T=%d is negative", T);
-  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_DECODE_INT8)
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL_INT8)
     return fail(BITMOE_EINVAL, "bitmoe_workspace_size: unknown mode %d", mode);
   *bytes = ws_bytes_for(L, T, mode);
   return BITMOE_OK;
@@ -392,9 +429,9 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
   if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
   if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
-  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_DECODE_INT8)
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL_INT8)
     return fail(BITMOE_EINVAL, "%s: unknown mode %d", fn, mode);
-  if (mode == BITMOE_MODE_DECODE_INT8 && L->d_ff < 256)
+  if ((mode == BITMOE_MODE_DECODE_INT8 || mode == BITMOE_MODE_PREFILL_INT8) && L->d_ff < 256)
     return fail(BITMOE_EUNSUPPORTED, "%s: int8 numerics need d_ff >= 256 (got %d)", fn, L->d_ff);
   if (T == 0) return BITMOE_OK;
   const int m = resolve_mode(mode, T);
@@ -419,6 +456,34 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   if (m == BITMOE_MODE_DECODE_INT8) {
     const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status, true);
     hipError_t e = bm::launch_decode_ffn_i8(a, x_dtype == BITMOE_F32, stream);
+    if (e != hipSuccess) return hip_fail(fn, e);
+    return BITMOE_OK;
+  }
+  if (m == BITMOE_MODE_PREFILL_INT8) {
+    bm::PrefillI8Args a{};
+    carve_prefill_i8(c, L, T, &a);
+    a.D = L->d_model;
+    a.F = L->d_ff;
+    a.E = L->n_experts;
+    a.k = L->top_k;
+    a.T = T;
+    a.wg = static_cast<const uint8_t *>(L->w_gate);
+    a.wu = static_cast<const uint8_t *>(L->w_up);
+    a.wd = static_cast<const uint8_t *>(L->w_down);
+    a.sg = shared ? static_cast<const uint8_t *>(L->ws_gate) : nullptr;
+    a.su = shared ? static_cast<const uint8_t *>(L->ws_up) : nullptr;
+    a.sd = shared ? static_cast<const uint8_t *>(L->ws_down) : nullptr;
+    a.x = x;
+    a.x_f32 = x_dtype == BITMOE_F32;
+    a.ids = topk_ids;
+    a.wts = topk_w;
+    a.plan.status = status;
+    a.out = y;
+    a.out_bf16 = y_dtype == BITMOE_BF16;
+    a.status = status;
+    hipError_t e = bm::launch_prefill_ffn_i8(a, stream);
+    if (e == hipErrorNotSupported)
+      return fail(BITMOE_EUNSUPPORTED, "%s: int8 prefill path not available for this shape", fn);
     if (e != hipSuccess) return hip_fail(fn, e);
     return BITMOE_OK;
   }

@@ -125,6 +125,35 @@ struct PrefillArgs {
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
 // routed grouped GEMM (gate/up with h out, or down with y out) over the plan's
 // chunks, after the activation rows' sub-block sums (into sums)
+// Int8 numerics of the prefill path (prefill_i8.hip)
+struct PrefillI8Args {
+  int D, F, E, k, T;
+  const uint8_t *wg, *wu, *wd;
+  const uint8_t *sg, *su, *sd;
+  const void *x;
+  bool x_f32;
+  const int32_t *ids;
+  const float *wts;
+  PlanBufs plan;
+  int32_t *tile_off, *tile_off2;  // chunk lists of the plan (PREFILL_BM, PREFILL_BM_DOWN rows)
+  int8_t *xq;                     // [T][D] quantised x, with its block scales [T][D/32] and stored sums [T][D/16]
+  float *xd, *xs;
+  uint16_t *sums;                 // stored sums in the min-term layout: max(T*D, T*k*F) / 8 bf16
+  float *hf;                      // [T*k][F] h in float32 (pair order)
+  int8_t *hq;                     // [T*k][F] quantised h, scales [T*k][F/32], sums [T*k][F/16]
+  float *hd, *hs;
+  int8_t *sw_i8;                  // [3][F*D] int8 codes of the shared expert (gate, up, down)
+  float *sw_d;                    // [3][F*D/32] their scales
+  float *hsf;                     // [T][F] shared h in float32
+  int8_t *hsq;                    // [T][F] quantised, scales [T][F/32], sums [T][F/16]
+  float *hsd, *hss;
+  float *y;                       // [T*k][D] float32, pair order
+  float *ys;                      // [T][D]
+  void *out;
+  int out_bf16;
+  int64_t *status;
+};
+hipError_t launch_prefill_ffn_i8(const PrefillI8Args &a, hipStream_t stream);
 hipError_t launch_probe_mfma(int blocks, int iters, uint32_t *sink, hipStream_t stream);
 hipError_t launch_q2_group(bool gateup, const PrefillArgs &a, const uint16_t *x, uint16_t *sums, float *tot,
                            hipStream_t stream);

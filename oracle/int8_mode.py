@@ -62,6 +62,32 @@ def quantize_blocks(v) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return q.reshape(*lead, -1).astype(np.int8), d, s
 
 
+def _q2_parse(raw: np.ndarray, n_rows: int, n_cols: int):
+    """The fields of a row-major [n_rows][n_cols] Q2 matrix, per sub-block of
+    the flattened matrix: codes [nsub][16], sc, m, and d, dmin of its
+    super-block."""
+    if n_cols % QBLOCK:
+        raise ValueError("n_cols must be a multiple of 32")
+    qw, sc, m, d, dmin = formats.q2_fields(np.asarray(raw, dtype=np.uint8).reshape(-1, formats.Q2_BLOCK_BYTES))
+    nsub = n_rows * n_cols // HALF                       # sub-blocks of the flattened matrix
+    sb = np.arange(nsub) // 16                             # super-block of each sub-block
+    return (qw.reshape(nsub, HALF).astype(np.int64), sc.reshape(-1).astype(np.float64),
+            m.reshape(-1).astype(np.float64), d[sb], dmin[sb], n_rows, n_cols)
+
+
+def _q2_dot(parsed, q, dx, s) -> np.ndarray:
+    qw, sc, m, d, dmin, n_rows, n_cols = parsed
+    nsub = qw.shape[0]
+    per_row = n_cols // HALF
+    j = np.arange(nsub) % per_row                          # sub-block's column group in its row
+    qa = np.asarray(q, dtype=np.int64).reshape(per_row, HALF)
+    dots = np.einsum("bk,bk->b", qw, qa[j])              # exact integer sums
+    dxb = np.asarray(dx, dtype=np.float64)[j // 2]
+    sj = np.asarray(s, dtype=np.float64)[j]
+    term = d * (sc * dxb * dots) - dmin * (m * sj)
+    return term.reshape(n_rows, per_row).sum(-1)
+
+
 def q2_rows_dot(raw: np.ndarray, n_rows: int, n_cols: int, q, dx, s) -> np.ndarray:
     """Rows of a row-major [n_rows][n_cols] Q2 matrix against one quantised
     activation vector (q [n_cols] int8, dx [n_cols/32], s [n_cols/16]).
@@ -71,20 +97,7 @@ def q2_rows_dot(raw: np.ndarray, n_rows: int, n_cols: int, q, dx, s) -> np.ndarr
     shares a super-block with the next row); every 16-weight sub-block lies in
     one row, and its columns in one activation block since n_cols is a
     multiple of 32."""
-    if n_cols % QBLOCK:
-        raise ValueError("n_cols must be a multiple of 32")
-    qw, sc, m, d, dmin = formats.q2_fields(np.asarray(raw, dtype=np.uint8).reshape(-1, formats.Q2_BLOCK_BYTES))
-    nsub = n_rows * n_cols // HALF                       # sub-blocks of the flattened matrix
-    qw = qw.reshape(nsub, HALF).astype(np.int64)
-    per_row = n_cols // HALF
-    j = np.arange(nsub) % per_row                          # sub-block's column group in its row
-    qa = np.asarray(q, dtype=np.int64).reshape(per_row, HALF)
-    dots = np.einsum("bk,bk->b", qw, qa[j])              # exact integer sums
-    sb = np.arange(nsub) // 16                             # super-block of each sub-block
-    dxb = np.asarray(dx, dtype=np.float64)[j // 2]
-    sj = np.asarray(s, dtype=np.float64)[j]
-    term = d[sb] * (sc.reshape(-1).astype(np.float64) * dxb * dots) - dmin[sb] * (m.reshape(-1).astype(np.float64) * sj)
-    return term.reshape(n_rows, per_row).sum(-1)
+    return _q2_dot(_q2_parse(raw, n_rows, n_cols), q, dx, s)
 
 
 def q8_0_rows_dot(raw: np.ndarray, n_rows: int, n_cols: int, q, dx) -> np.ndarray:
@@ -117,6 +130,21 @@ def ffn_int8(layer: moe.Layer, e: int, x_row) -> tuple[np.ndarray, np.ndarray]:
     h = moe.silu(g) * u
     ha = quantize_blocks(h.astype(np.float32))
     return _matrix_dot(layer, "down", e, ha), h
+
+
+def ffn_int8_rows(layer: moe.Layer, e: int, X) -> np.ndarray:
+    """ffn_int8 of routed expert e for each row of X (float32 values), each
+    matrix parsed once.  Returns y float64 [rows][d_model]."""
+    D, F = layer.d_model, layer.d_ff
+    pg = _q2_parse(layer.expert_bytes("gate", e), F, D)
+    pu = _q2_parse(layer.expert_bytes("up", e), F, D)
+    pd = _q2_parse(layer.expert_bytes("down", e), D, F)
+    out = np.zeros((len(X), D))
+    for i, x_row in enumerate(X):
+        xa = quantize_blocks(np.asarray(x_row, dtype=np.float32))
+        h = moe.silu(_q2_dot(pg, *xa)) * _q2_dot(pu, *xa)
+        out[i] = _q2_dot(pd, *quantize_blocks(h.astype(np.float32)))
+    return out
 
 
 def moe_layer_int8(layer: moe.Layer, x: np.ndarray, bias=None, ids=None) -> moe.LayerResult:

@@ -151,7 +151,7 @@ def test_expert_ffn_rejects_bad_args(lib):
     assert lib.moe_expert_ffn(*args(ws=P(0x10010), wsb=1 << 40)) == bm.EINVAL  # not 256-aligned
     assert lib.moe_expert_ffn(*args(T=9, mode=bm.MODE_DECODE, wsb=1 << 40)) == bm.EUNSUPPORTED
     assert lib.moe_expert_ffn(*args(T=9, mode=bm.MODE_DECODE_INT8, wsb=1 << 40)) == bm.EUNSUPPORTED
-    assert lib.moe_expert_ffn(*args(mode=4, wsb=1 << 40)) == bm.EINVAL
+    assert lib.moe_expert_ffn(*args(mode=6, wsb=1 << 40)) == bm.EINVAL  # 4 is MODE_PREFILL_INT8
     assert lib.moe_expert_ffn(*args(mode=bm.MODE_DECODE_INT8, wsb=64)) == bm.EWORKSPACE
     assert lib.moe_expert_ffn(*args(T=0, x=None, y=None)) == bm.OK
 
@@ -163,7 +163,7 @@ def test_int8_mode_workspace_and_shape_limits(lib):
     assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, bm.MODE_DECODE, ctypes.byref(n1)) == bm.OK
     # float32 h in place of its two bf16 parts: the same size
     assert n8.value == n1.value
-    assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, 4, ctypes.byref(n8)) == bm.EINVAL
+    assert lib.bitmoe_workspace_size(ctypes.byref(L), 5, 6, ctypes.byref(n8)) == bm.EINVAL
     # the int8 mode needs d_ff >= 256 (two 16-value halves per 32-value block of h, whole super-blocks per row)
     Ls = _layer(d_ff=128)
     P = ctypes.c_void_p

@@ -60,18 +60,18 @@ def test_quantizer_bit_exact_bf16_and_ragged_rows():
         _quant_check(x_np, x_dev)
 
 
-def _int8_layer(ld, T, tag, out_dtype, ids_override=None):
+def _int8_layer(ld, T, tag, out_dtype, ids_override=None, mode=bm.MODE_DECODE_INT8):
     cfg = ld.cfg
     layer = device_layer(ld, host_bytes=cfg.n_experts * ld.blocks_per_expert < 200000)
     x = x_device(ld, tag, T)
-    ws = bm.workspace(layer, T, bm.MODE_DECODE_INT8)
+    ws = bm.workspace(layer, T, mode)
     ids, w = bm.route(layer, x, ws)
     xv = ld.x_values(tag, T)
     if ids_override is not None:
         _, _, L = moe.route(xv, ld.router(), cfg.top_k)
         ids = torch.from_numpy(ids_override.astype(np.int32)).cuda()
         w = torch.from_numpy(moe.weights_for_selection(L, ids_override).astype(np.float32)).cuda()
-    y = bm.expert_ffn(layer, x, ids, w, ws, out_dtype=out_dtype, mode=bm.MODE_DECODE_INT8)
+    y = bm.expert_ffn(layer, x, ids, w, ws, out_dtype=out_dtype, mode=mode)
     torch.cuda.synchronize()
     ids_h = ids.cpu().numpy()
     ref = int8_mode.moe_layer_int8(oracle_layer(ld), xv, ids=ids_h)
@@ -80,7 +80,7 @@ def _int8_layer(ld, T, tag, out_dtype, ids_override=None):
         assert not compare.compare_ids(ids_h, r_ids, L)[2]
     yv = y.float().cpu().numpy().astype(np.float64)
     err = compare.max_rel_error(yv, ref.out)
-    print(f"[parity] int8 {cfg.name} T={T} out={out_dtype} max rel err {err:.3e} "
+    print(f"[parity] int8 mode {mode} {cfg.name} T={T} out={out_dtype} max rel err {err:.3e} "
           f"normwise {compare.normwise_rel_error(yv, ref.out):.3e}")
     assert bm.read_status(bm.ws_status(ws))[0] == 0
     return err, y, ref
@@ -165,7 +165,8 @@ def test_int8_deterministic():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-@pytest.mark.parametrize("mode", [bm.MODE_AUTO, bm.MODE_DECODE, bm.MODE_PREFILL, bm.MODE_DECODE_INT8])
+@pytest.mark.parametrize("mode", [bm.MODE_AUTO, bm.MODE_DECODE, bm.MODE_PREFILL, bm.MODE_DECODE_INT8,
+                                  bm.MODE_PREFILL_INT8])
 def test_empty_batch_every_mode(mode):
     # T = 0: the router and the expert call launch nothing and return empty outputs
     ld = synthdata.LayerData(SMALL, 25)
@@ -177,3 +178,85 @@ def test_empty_batch_every_mode(mode):
     torch.cuda.synchronize()
     assert ids.shape == (0, SMALL.top_k) and w.shape == (0, SMALL.top_k) and y.shape == (0, SMALL.d_model)
     assert bm.read_status(bm.ws_status(ws))[0] == 0
+
+
+
+# ---------------------------------------------------------------- prefill (int8 MFMA)
+
+PF_SMALL = synthdata.Config("int8-pf-small", 300, 512, 256, 16, 2, "bf16", True, zipf_lambda=1.0)
+
+
+@pytest.mark.parametrize("T", [1, 8, 129, 300])
+def test_prefill_int8_small_layer(T):
+    # chunks of one token up to several 48-token chunks per expert, ragged tails
+    ld = synthdata.LayerData(PF_SMALL, 31)
+    err, _, _ = _int8_layer(ld, T, 80 + T, torch.float32, mode=bm.MODE_PREFILL_INT8)
+    assert err < TOL_F32
+
+
+def test_prefill_int8_f32_activations_bf16_out():
+    cfg = synthdata.Config("int8-pf-f32", 96, 512, 256, 16, 2, "f32", True)
+    ld = synthdata.LayerData(cfg, 32)
+    err, _, _ = _int8_layer(ld, 96, 5, torch.bfloat16, mode=bm.MODE_PREFILL_INT8)
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("T", [1, 5, 8])
+def test_prefill_int8_agrees_with_decode_int8(T):
+    # the same numerics on both paths: equal up to float32 rounding order (and
+    # the rare h code that such rounding moves across a quantiser boundary)
+    ld = synthdata.LayerData(synthdata.CONFIGS["decode"], 33)
+    layer = device_layer(ld)
+    x = x_device(ld, 90 + T, T)
+    ws = bm.workspace(layer, T, bm.MODE_PREFILL_INT8)
+    ids, w = bm.route(layer, x, ws)
+    yp = bm.expert_ffn(layer, x, ids, w, ws, out_dtype=torch.float32, mode=bm.MODE_PREFILL_INT8).clone()
+    ws2 = bm.workspace(layer, T, bm.MODE_DECODE_INT8)
+    yd = bm.expert_ffn(layer, x, ids, w, ws2, out_dtype=torch.float32, mode=bm.MODE_DECODE_INT8)
+    torch.cuda.synchronize()
+    err = compare.max_rel_error(yp.cpu().numpy().astype(np.float64), yd.cpu().numpy().astype(np.float64))
+    print(f"[parity] prefill int8 vs decode int8 T={T}: max rel diff {err:.3e}")
+    assert err < TOL_F32
+
+
+def test_prefill_int8_full_shape_pairs_and_determinism():
+    """The 4096-token chunk (Zipf-biased routing): per-pair float32 outputs of
+    a few experts' every pair (one-hot mixing weights, no shared expert) against
+    the oracle, and the same call twice bit for bit."""
+    import dataclasses
+    cfg = dataclasses.replace(synthdata.CONFIGS["prefill"], shared=False)
+    ld = synthdata.LayerData(cfg, 1)
+    layer = device_layer(ld)
+    x = x_device(ld)
+    ws = bm.workspace(layer, cfg.T, bm.MODE_PREFILL_INT8)
+    ids, _ = bm.route(layer, x, ws, bias=torch.from_numpy(ld.bias()).cuda())
+    ids_h = ids.cpu().numpy()
+    counts = np.bincount(ids_h.reshape(-1), minlength=cfg.n_experts)
+    used = np.nonzero(counts)[0]
+    small = used[np.argsort(counts[used])[:3]]        # the three smallest groups (single-tile chunks)
+    mid = used[np.argsort(counts[used])[len(used) // 2]]
+    chosen = [int(e) for e in small] + [int(mid)]
+    outs = []
+    for j in range(cfg.top_k):
+        w = torch.zeros((cfg.T, cfg.top_k), dtype=torch.float32, device="cuda")
+        w[:, j] = 1.0
+        outs.append(bm.expert_ffn(layer, x, ids, w, ws, out_dtype=torch.float32, mode=bm.MODE_PREFILL_INT8).cpu().numpy())
+    w = torch.zeros((cfg.T, cfg.top_k), dtype=torch.float32, device="cuda")
+    w[:, 0] = 1.0
+    again = bm.expert_ffn(layer, x, ids, w, ws, out_dtype=torch.float32, mode=bm.MODE_PREFILL_INT8).cpu().numpy()
+    assert np.array_equal(again.view(np.uint32), outs[0].view(np.uint32))
+    Y = np.stack(outs, axis=1)
+    ol = oracle_layer(ld)
+    xv = ld.x_values().astype(np.float32)
+    worst, n = 0.0, 0
+    for e in chosen:
+        toks, slots = np.nonzero(ids_h == e)
+        ref = int8_mode.ffn_int8_rows(ol, e, xv[toks])
+        err = compare.max_rel_error(Y[toks, slots].astype(np.float64), ref)
+        print(f"[parity] int8 prefill expert {e}: {len(toks)} pairs, max rel err {err:.3e}", flush=True)
+        worst, n = max(worst, err), n + len(toks)
+    assert n >= 60
+    # at d_ff 2048 one h code moved across a quantiser boundary (see the top)
+    # moves an element by up to (max|h| / 127) max|w| / rms(y), ~5e-3 here, so
+    # the elementwise bar at this shape is the bf16 one
+    assert worst < TOL_BF16

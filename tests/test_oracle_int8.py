@@ -163,3 +163,14 @@ def test_ffn_int8_requantises_h_hand_worked():
     assert math.isclose(y[0], 169 * d_h, rel_tol=1e-12), (y[0], 169 * d_h)
     assert abs(y[0] - (h0 + h0 / 3)) > 1e-3 * abs(y[0])  # h is not used unquantised
     assert np.all(y[1:] == 0)
+
+
+def test_ffn_int8_rows_equals_per_token_ffn():
+    # the batched form parses each matrix once and runs the same arithmetic
+    cfg = synthdata.Config("i8rows", 3, 256, 256, 4, 2, "f32", False)
+    ld = synthdata.LayerData(cfg, 5)
+    layer = moe.Layer(cfg.d_model, cfg.d_ff, cfg.n_experts, cfg.top_k, ld.router(), ld.expert_bytes)
+    X = ld.x_values(2).astype(np.float32)
+    got = int8_mode.ffn_int8_rows(layer, 2, X)
+    for i in range(len(X)):
+        assert np.array_equal(got[i], int8_mode.ffn_int8(layer, 2, X[i])[0])
