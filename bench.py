@@ -66,9 +66,16 @@ def algorithmic_bytes(T: int, U: float, D: int = 4096, F: int = 2048, E: int = 3
     }
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# the decode GEMV kernels' own sources: the stored counter figures describe these
+DECODE_KERNEL_SOURCES = ("gemv.hip", "gemv_units.h", "decode_job.h")
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in ([paths] if isinstance(paths, str) else paths):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel_src: str, label: str):
@@ -684,7 +691,7 @@ def main() -> int:
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
     dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
     achieved = alg[dom] / dom_avg_s / 1e9
-    src = os.path.join(ROOT, "bit_moe_amd", "csrc", "gemv.hip")
+    src = [os.path.join(ROOT, "bit_moe_amd", "csrc", f) for f in DECODE_KERNEL_SOURCES]
     traffic = stored_traffic(src, dom)
     step_ms = (graph_ms if graph_ms is not None else eager_ms) / K
     value = T / (step_ms * 1e-3)
