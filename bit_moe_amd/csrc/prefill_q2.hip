@@ -16,11 +16,17 @@
 // expert's tokens -- up to three 16-token M-tiles for gate/up, two for down,
 // as many as the chunk needs -- and one N-tile of 256 weight rows (8 waves of
 // 2 x 16 rows); each wave builds the operands of its weight rows for a whole
-// 256-wide K-step once and applies them to every M-tile of the chunk.  The chunk's activation rows (double-buffered) and
-// their sub-block sums (precomputed once per call by xsum_kernel) are staged
-// in LDS with direct-to-LDS copies one K-step ahead; each lane's weight bytes
-// for the next step are loaded into registers.  Padding is per 16-token tile:
-// a group of n tokens runs ceil(n / 16) tiles.
+// 256-wide K-step once and applies them to every M-tile of the chunk.  The
+// chunk's activation rows and their sub-block sums (precomputed once per call
+// by xsum_kernel) are staged in LDS with direct-to-LDS copies one K-step
+// ahead, double-buffered.  Gate/up stages the step's weight bytes the same
+// way (16-byte copies of consecutive rows' super-blocks: each copy instruction
+// reads about four contiguous 84-byte runs, where per-lane loads of a lane's
+// own 28 bytes touch sixteen rows per instruction, and were measured 0.25 ms
+// slower on the 4096-token chunk); down, whose two activation parts take
+// twice the LDS per row, loads each lane's weight bytes into registers and
+// keeps two blocks per CU.  Padding is per 16-token tile: a group of n tokens
+// runs ceil(n / 16) tiles.
 //
 //  gate/up  (GATEUP): weight rows of the gate and up matrices alike, h =
 //           silu(g) u stored as bf16 hi + lo parts per pair.
@@ -35,7 +41,10 @@ namespace bm {
 namespace {
 
 constexpr int KS = 256;               // K per step (one super-block of every weight row)
-constexpr int ROWP = KS + 8;          // bf16 per LDS activation row (16-byte pad)
+#ifndef BM_PF_ROWPAD
+#define BM_PF_ROWPAD 8
+#endif
+constexpr int ROWP = KS + BM_PF_ROWPAD;  // bf16 per LDS activation row (16-byte pad)
 constexpr int SUMS = 32;              // bf16 sums per (row, step): 16 sub-blocks x (hi, lo)
 constexpr int MT_GU = BM_PF_CHUNK_GU;  // gate/up: M-tiles of 16 per chunk
 constexpr int MT_DN = BM_PF_CHUNK_DN;  // down: M-tiles of 16 pairs per chunk (hi and lo rows: twice the LDS per row)
@@ -115,8 +124,22 @@ struct GroupGeo {
   static constexpr int BUF = PARTS * 16 * MT * ROWP * 2;  // bytes of one activation buffer
   static constexpr int SBUF = 16 * MT * SUMS * 2;         // bytes of one sums buffer
   static constexpr int TBUF = 16 * MT * 4;                // bytes of one buffer of super-block totals
-  static constexpr int ROWS_OFF = 2 * BUF + 2 * SBUF + 2 * TBUF;  // chunk row table
+  // gate/up stages one step's weights per matrix in LDS: bytes 0..79 of every
+  // row's super-block (codes and scales) as 5 16-byte pieces per row, then the
+  // rows' d|dmin words.  Down loads them into registers instead (its LDS then
+  // holds two blocks per CU, four waves per SIMD).
+  static constexpr bool WLDS = GATEUP;
+  static constexpr int WMAT = BN * 84;                    // bytes per matrix and step
+  static constexpr int WBUF = WLDS ? NM * WMAT : 0;
+  static constexpr int WX4 = BN * 5 / 64;                 // 64-lane 16-byte copies per matrix and step
+  static constexpr int WX1 = BN / 64;                     // 64-lane dword copies (d|dmin) per matrix and step
+  static constexpr int WPM = WAVES / NM;                  // waves copying one matrix
+  static constexpr int WC4 = (WX4 + WPM - 1) / WPM;       // 16-byte copies per wave and step
+  static constexpr int WC1 = (WX1 + WPM - 1) / WPM;       // dword copies per wave and step
+  static constexpr int ROWS_OFF = 2 * BUF + 2 * SBUF + 2 * TBUF + 2 * WBUF;  // chunk row table
   static constexpr size_t SMEM = size_t(ROWS_OFF) + 16 * MT * 4;
+  static_assert(BN * 5 % 64 == 0 && BN % 64 == 0 && WAVES % NM == 0, "weight copies of whole 64-lane rows");
+  static_assert(SMEM <= 160 * 1024, "LDS of one CU");
 };
 
 template <bool GATEUP, int NT>
@@ -126,15 +149,34 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
   uint8_t *abuf = smem;
   uint8_t *sbuf = smem + 2 * Gm::BUF;
   uint8_t *tbuf = sbuf + 2 * Gm::SBUF;
+  uint8_t *wbuf = tbuf + 2 * Gm::TBUF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, nl = lane & 15, p = gq & 1;
   const int nsteps = g.K / KS;
   const size_t row_bytes = size_t(nsteps) * 84;
   const int n_w = ntile * Gm::BN + wave * 16 * NG + nl;  // weight row of group 0; group ng adds 16 ng
   constexpr int W = Gm::WAVES;
+  // weight copies: wave `wave` copies matrix wm; its 16-byte copy c moves
+  // pieces 64 j + l (lane l, j = wj0 + WPM c) of the step image, piece i being
+  // bytes 16 (i % 5) .. +15 of row i / 5's super-block; its dword copy moves
+  // the d|dmin words of rows 64 j + l.  Source offsets (from the block's first
+  // row, step 0) do not depend on the step.
+  const int wm = wave / Gm::WPM, wj0 = wave % Gm::WPM;
+  const uint8_t *wsrc = (wm ? g.b1 : g.b0) + size_t(e) * g.b_stride + size_t(ntile) * Gm::BN * row_bytes;
+  uint32_t woff4[Gm::WC4], woff1[Gm::WC1];
+  // register path (down): the lane's own rows
   const uint8_t *wb[NM];
   wb[0] = g.b0 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
   if constexpr (GATEUP) wb[1] = g.b1 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
+#pragma unroll
+  for (int c = 0; c < Gm::WC4; ++c) {
+    const int i = 64 * min(wj0 + Gm::WPM * c, Gm::WX4 - 1) + lane;
+    const int row = i / 5;
+    woff4[c] = uint32_t(row) * uint32_t(row_bytes) + 16u * uint32_t(i - 5 * row);
+  }
+#pragma unroll
+  for (int c = 0; c < Gm::WC1; ++c)
+    woff1[c] = uint32_t(64 * min(wj0 + Gm::WPM * c, Gm::WX1 - 1) + lane) * uint32_t(row_bytes) + 80u;
   // copies of step kb into buffer half: activation rows (512 B each, half a
   // wave per row; this wave's rows wave, wave + W, ..) and their sums (64 B
   // per row, 16 rows per instruction).  Addresses are formed in vector
@@ -159,12 +201,38 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
       const int src = rows[lane];
       if (src >= 0) lds_dma4(g.tot + size_t(src) * nsteps + kb, lds_offset(tbuf + half * Gm::TBUF));
     }
+    if constexpr (!Gm::WLDS) return;
+    uint8_t *wd = wbuf + half * Gm::WBUF + wm * Gm::WMAT;
+    const uint8_t *ws = wsrc + size_t(kb) * 84;
+#pragma unroll
+    for (int c = 0; c < Gm::WC4; ++c) {
+      const int j = wj0 + Gm::WPM * c;
+      if (Gm::WX4 % Gm::WPM == 0 || j < Gm::WX4) lds_dma16(ws + woff4[c], lds_offset(wd + 1024 * j));
+    }
+#pragma unroll
+    for (int c = 0; c < Gm::WC1; ++c) {
+      const int j = wj0 + Gm::WPM * c;
+      if (Gm::WX1 % Gm::WPM == 0 || j < Gm::WX1) lds_dma4(ws + woff1[c], lds_offset(wd + Gm::BN * 80 + 256 * j));
+    }
   };
   auto load_b = [&](int kb, Q2Raw (&raw)[NG][NM]) {
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
       for (int m = 0; m < NM; ++m) raw[ng][m] = q2_load(wb[m] + size_t(16 * ng) * row_bytes + size_t(kb) * 84, gq);
+  };
+  // this lane's raw bytes of group ng, matrix m from the step image
+  auto read_b = [&](int half, Q2Raw (&raw)[NG][NM]) {
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint8_t *wm_ = wbuf + half * Gm::WBUF + m * Gm::WMAT;
+        const int r = wave * 16 * NG + 16 * ng + nl, h = gq >> 1;
+        raw[ng][m].q = *reinterpret_cast<const q2u32x4 *>(wm_ + 80 * r + 16 + 32 * h + 16 * p);
+        raw[ng][m].sc = *reinterpret_cast<const q2u32x2 *>(wm_ + 80 * r + 8 * h);
+        raw[ng][m].dd = *reinterpret_cast<const uint32_t *>(wm_ + Gm::BN * 80 + 4 * r);
+      }
   };
   f32x4_t acc[NT][NG][NM];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -176,20 +244,23 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
       for (int m = 0; m < NM; ++m) acc[mi][ng][m] = zero;
   Q2Raw cur[NG][NM];
   issue(0, 0);
-  load_b(0, cur);
+  if constexpr (!Gm::WLDS) load_b(0, cur);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (!Gm::WLDS) {
 #pragma unroll
-  for (int ng = 0; ng < NG; ++ng)
+    for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-    for (int m = 0; m < NM; ++m) q2_settle(cur[ng][m]);
+      for (int m = 0; m < NM; ++m) q2_settle(cur[ng][m]);
+  }
   __syncthreads();
   for (int kb = 0; kb < nsteps; ++kb) {
     const int half = kb & 1;
     Q2Raw nxt[NG][NM];
     if (kb + 1 < nsteps) {
       issue(kb + 1, half ^ 1);
-      load_b(kb + 1, nxt);
+      if constexpr (!Gm::WLDS) load_b(kb + 1, nxt);
     }
+    if constexpr (Gm::WLDS) read_b(half, cur);
     const uint16_t *Ah = reinterpret_cast<const uint16_t *>(abuf + half * Gm::BUF);
     const uint16_t *Sx = reinterpret_cast<const uint16_t *>(sbuf + half * Gm::SBUF);
     const float *Xt = reinterpret_cast<const float *>(tbuf + half * Gm::TBUF);
@@ -247,18 +318,20 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
       }
     }
     if (kb + 1 < nsteps) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows, sums and weight bytes have landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows, sums, totals and weights have landed
       __syncthreads();                                  // ... and this step's buffers are no longer read
-      // the weight bytes count as produced by the wait above, so the compiler
-      // keeps no load of them pending (a pending load would make it wait again
-      // in the next step, behind that step's copies)
+      if constexpr (!Gm::WLDS) {
+        // the weight bytes count as produced by the wait above, so the
+        // compiler keeps no load of them pending (a pending load would make it
+        // wait again in the next step, behind that step's copies)
 #pragma unroll
-      for (int ng = 0; ng < NG; ++ng)
+        for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          q2_settle(nxt[ng][m]);
-          cur[ng][m] = nxt[ng][m];
-        }
+          for (int m = 0; m < NM; ++m) {
+            q2_settle(nxt[ng][m]);
+            cur[ng][m] = nxt[ng][m];
+          }
+      }
     }
   }
   // epilogue: lane holds rows 16 mi + 4 gq + r of column n_w + 16 ng
