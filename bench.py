@@ -6,7 +6,9 @@ Workload (the single-layer decode configuration): T = 1 token, d_model 4096,
 every expert matrix in the 2-bit super-block format, one Q8_0 shared expert,
 bf16 activations.  A step is one pass of the hot path for one token: router
 (logits, top-6, weights) + gate/up GEMV with SwiGLU + down GEMV + combine, all
-HIP kernels of libbitmoe behind its C ABI.
+HIP kernels of libbitmoe behind its C ABI, issued by one moe_layer call (four
+launches: router, gate/up whose routed blocks select their experts from the
+logits, down, combine).
 
 Inputs are seeded and synthetic and resident in HBM before timing.  To keep
 the 256 MB Infinity Cache from serving re-reads, the steps rotate through 16
@@ -51,9 +53,10 @@ def log(msg: str) -> None:
 
 def algorithmic_bytes(T: int, U: float, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
     """Bytes the method must move per launch of each decode kernel that runs at
-    T tokens with U distinct experts: the router, the top-k, the gate/up and
-    down GEMV launches (each holding the routed experts' and the shared
-    expert's rows) and the combine.  h travels as bf16 hi + lo."""
+    T tokens with U distinct experts (moe_route + moe_expert_ffn): the router,
+    the top-k, the gate/up and down GEMV launches (each holding the routed
+    experts' and the shared expert's rows) and the combine.  h travels as bf16
+    hi + lo."""
     P = T * k
     x = T * D * 2
     h_pairs, h_tok = P * F * 2 * 2, T * F * 2 * 2
@@ -66,8 +69,21 @@ def algorithmic_bytes(T: int, U: float, D: int = 4096, F: int = 2048, E: int = 3
     }
 
 
+def algorithmic_bytes_layer(U: float, D: int = 4096, F: int = 2048, E: int = 384, k: int = 6) -> dict:
+    """The same for moe_layer at T = 1: no top-k launch; the gate/up launch also
+    reads the logits (its routed blocks select the experts) and writes the
+    selection."""
+    two = algorithmic_bytes(1, U, D, F, E, k)
+    return {
+        "router_gemv_kernel": two["router_gemv_kernel"],
+        "ffn_gateup_kernel": two["ffn_gateup_kernel"] + E * 4 + k * 8,
+        "ffn_down_kernel": two["ffn_down_kernel"],
+        "combine_kernel": two["combine_kernel"],
+    }
+
+
 # the decode GEMV kernels' own sources: the stored counter figures describe these
-DECODE_KERNEL_SOURCES = ("gemv.hip", "gemv_units.h", "decode_job.h")
+DECODE_KERNEL_SOURCES = ("gemv.hip", "gemv_units.h", "decode_job.h", "router_units.h")
 
 
 def source_hash(paths) -> str:
@@ -521,8 +537,7 @@ def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
         def step(i):
             x = xs[i]
             for l, L in enumerate(layers):
-                bm.route(L, x, ws, ids=ids, weights=wts)
-                bm.expert_ffn(L, x, ids, wts, ws, y=y, mode=mode)
+                bm.layer(L, x, ws, ids=ids, weights=wts, y=y, mode=mode)
                 if l in tables:
                     t, j = tables[l]
                     bm.engram_gather(t, rid[i][j], out=rows)
@@ -549,7 +564,8 @@ def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
             x = bm.residual_rescale(x, y)
         del ws
         for u in U:
-            per_layer += sum(algorithmic_bytes(T, u).values()) + 3 * T * D * 2  # + residual step
+            kb = algorithmic_bytes_layer(u) if T == 1 else algorithmic_bytes(T, u)
+            per_layer += sum(kb.values()) + 3 * T * D * 2  # + residual step
         eng = len(cfg.engram_layers) * (T * 8 * (264 + 512) + T * 8 * 8)
         total = per_layer + eng
         out[f"decode_T{T}"] = {"tokens_per_s": round(T / (step_ms * 1e-3), 1), "ms_per_step": round(step_ms, 4),
@@ -610,7 +626,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--instances", type=int, default=16)
     ap.add_argument("--seed", type=int, default=1)
-    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--cpu-repeats", type=int, default=1)
     ap.add_argument("--verify-steps", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -675,9 +691,7 @@ def main() -> int:
     log(f"[bench] {NI} decode layer instances resident ({time.time() - t0:.1f} s)")
 
     def step(i: int) -> None:
-        L = layers[i % NI]
-        bm.route(L, xs[i], ws, ids=ids, weights=wts)
-        bm.expert_ffn(L, xs[i], ids, wts, ws, y=y, mode=bm.MODE_DECODE)
+        bm.layer(layers[i % NI], xs[i], ws, ids=ids, weights=wts, y=y, mode=bm.MODE_DECODE)
 
     graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, not args.no_graph)
     if graph_ms is not None:
@@ -687,7 +701,7 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     T, U = 1, cfg.top_k
-    alg = algorithmic_bytes(T, U)
+    alg = algorithmic_bytes_layer(U)
     dom = max(prof.items(), key=lambda kv: kv[1][0])[0]
     dom_avg_s = prof[dom][0] / prof[dom][1] * 1e-3
     achieved = alg[dom] / dom_avg_s / 1e9

@@ -34,7 +34,7 @@ EXPORTS = [
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
     "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size", "moe_route_noalloc",
-    "bitmoe_probe_mfma",
+    "bitmoe_probe_mfma", "moe_layer",
 ]
 
 
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route_noalloc": [LP, P, I32, I32, P, P, P, P],
         "moe_route_ex": [LP, P, I32, I32, ctypes.POINTER(_RouteOptsC), P, P, P, SZ, P],
         "moe_expert_ffn": [LP, P, I32, I32, P, P, P, I32, I32, P, SZ, P],
+        "moe_layer": [LP, P, I32, I32, P, P, P, P, I32, I32, P, SZ, P],
         "engram_gather": [P, I64, P, I64, P, P, P],
         "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "bitmoe_plan_workspace_size": [I32, I32, I32, ctypes.POINTER(SZ)],
@@ -275,6 +276,31 @@ def expert_ffn(layer: Layer, x: torch.Tensor, ids: torch.Tensor, weights: torch.
     _check(lib.moe_expert_ffn(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(ids), _ptr(weights), _ptr(y),
                               _dtype_code(y), mode, _ptr(ws), ws.numel(), _stream(stream)))
     return y
+
+
+def layer(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
+          ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
+          y: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16, mode: int = MODE_AUTO, stream=None):
+    """moe_layer: moe_route followed by moe_expert_ffn in one call (one token in
+    decode mode runs in four launches).  Returns (ids, weights, y)."""
+    lib = load()
+    _require(x, "x")
+    T = x.shape[0]
+    if ids is None:
+        ids = torch.empty((T, layer.top_k), dtype=torch.int32, device=x.device)
+    if weights is None:
+        weights = torch.empty((T, layer.top_k), dtype=torch.float32, device=x.device)
+    if y is None:
+        y = torch.empty((T, layer.d_model), dtype=out_dtype, device=x.device)
+    _require(ids, "ids", torch.int32)
+    _require(weights, "weights", torch.float32)
+    _require(y, "y")
+    if bias is not None:
+        _require(bias, "bias", torch.float32)
+    lc = layer.c()
+    _check(lib.moe_layer(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids), _ptr(weights),
+                         _ptr(y), _dtype_code(y), mode, _ptr(ws), ws.numel(), _stream(stream)))
+    return ids, weights, y
 
 
 def engram_inject_workspace_bytes(T: int, width: int) -> int:

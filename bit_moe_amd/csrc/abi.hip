@@ -528,6 +528,40 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   return BITMOE_OK;
 }
 
+int moe_layer(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const float *logit_bias,
+              int32_t *topk_ids, float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
+              hipStream_t stream) {
+  const char *fn = "moe_layer";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (mode < BITMOE_MODE_AUTO || mode > BITMOE_MODE_PREFILL_INT8)
+    return fail(BITMOE_EINVAL, "%s: unknown mode %d", fn, mode);
+  if (T != 1 || resolve_mode(mode, T) != BITMOE_MODE_DECODE || L->top_k > 8) {
+    // the two calls' launches in order
+    rc = moe_route(L, x, x_dtype, T, logit_bias, topk_ids, topk_w, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return moe_expert_ffn(L, x, x_dtype, T, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes, stream);
+  }
+  if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+  if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
+  if (!x || !aligned(x, 16)) return fail(BITMOE_EINVAL, "%s: x is NULL or not 16-byte aligned", fn);
+  if (!y || !aligned(y, 16)) return fail(BITMOE_EINVAL, "%s: y is NULL or not 16-byte aligned", fn);
+  if (!topk_ids || !topk_w || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(BITMOE_EINVAL, "%s: topk_ids/topk_w NULL or misaligned", fn);
+  if (logit_bias && !aligned(logit_bias, 4)) return fail(BITMOE_EINVAL, "%s: logit_bias misaligned", fn);
+  rc = check_ws(fn, L, T, BITMOE_MODE_DECODE, ws, ws_bytes);
+  if (rc) return rc;
+  Carve c(ws);
+  int64_t *status;
+  float *logits;
+  carve_common(c, L, T, &status, &logits);
+  const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
+  hipError_t e = bm::launch_decode_layer(a, x_dtype == BITMOE_F32, L->w_router, logit_bias, logits, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
 int engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n, uint16_t *out,
                   int64_t *status, hipStream_t stream) {
   const char *fn = "engram_gather";

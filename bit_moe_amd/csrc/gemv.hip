@@ -40,6 +40,7 @@
 
 #include "decode_job.h"
 #include "gemv_units.h"
+#include "router_units.h"
 
 namespace bm {
 
@@ -589,7 +590,6 @@ static hipError_t launch_down_gemv(FfnArgs a, hipStream_t stream) {
 constexpr int RING_BYTES = 13 * 1024;  // LDS ring per wave
 constexpr int STREAM_ROWS_GU = 8, STREAM_ROWS_SG = 8;   // rows per chunk, gate/up (routed, shared)
 constexpr int STREAM_ROWS_DN = 16, STREAM_ROWS_SD = 16;  // down
-constexpr int LAYER_ROWS_SG = 2, LAYER_ROWS_SD = 4;      // shared rows per wave beside the router / top-k
 
 template <int K, bool IS_Q8>
 struct StreamGeo {
@@ -884,6 +884,87 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
   else
     err = launch_decode_nt<NTOK, 2, 2, false>(a, stream);
   if (err != hipSuccess) return err;
+  return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
+                        stream);
+}
+
+// ---- one decode step of one token in four launches ---------------------------
+// moe_layer at T = 1 runs moe_route + moe_expert_ffn (decode mode) as
+//  (1) the router logits (router_gemv_kernel, one block per expert row);
+//  (2) ffn_gateup_sel_kernel: the gate/up launch of moe_expert_ffn, whose
+//      routed blocks first select the token's experts from the logits with the
+//      top-k routine of moe_route (the same code on the same logits: every
+//      block reaches the same selection; the first routed block stores it as
+//      the call's ids and weights), while the shared expert's blocks, which
+//      need no selection, start streaming at once;
+//  (3) the down launch and (4) the combine, as moe_expert_ffn runs them.
+// Every row and output goes through the same arithmetic as in the two
+// separate calls, so ids, weights and y agree bit for bit; the top-k launch,
+// whose latency the shared rows now cover, is gone.
+
+template <int PER, bool XF32>
+__global__ void __launch_bounds__(256) ffn_gateup_sel_kernel(FfnArgs a, const float *__restrict__ logits,
+                                                             int32_t *__restrict__ ids_out,
+                                                             float *__restrict__ wts_out) {
+  const int b = int(blockIdx.x) - a.chunks_sg;
+  if (b < 0) {  // shared expert: chunk blockIdx.x of its rows
+    Job job;
+    shared_job(a, job);
+    const int r_begin = blockIdx.x * a.rows_sg;
+    gateup_rows<1, XF32, true>(a, job, 0, 1, r_begin, min(a.F, r_begin + a.rows_sg));
+    return;
+  }
+  __shared__ int32_t s_ids[8];
+  __shared__ float s_wts[8];
+  if (threadIdx.x < 64) topk_token<PER>(logits, a.E, a.k, s_ids, s_wts, threadIdx.x);
+  __syncthreads();
+  if (b == 0 && int(threadIdx.x) < a.k) {
+    ids_out[threadIdx.x] = s_ids[threadIdx.x];
+    wts_out[threadIdx.x] = s_wts[threadIdx.x];
+  }
+  a.ids = s_ids;
+  a.wts = s_wts;
+  Job job;
+  if (!pair_job_wave(a, b / a.chunks_gu, job)) return;
+  const int r_begin = (b % a.chunks_gu) * a.rows_gu;
+  gateup_rows<1, XF32, false>(a, job, 0, 1, r_begin, min(a.F, r_begin + a.rows_gu));
+}
+
+// a: the moe_expert_ffn arguments for one token with a.ids / a.wts the call's
+// outputs; wr, bias, logits: moe_route's router matrix, optional bias and
+// logit buffer ([E] float32).
+hipError_t launch_decode_layer(FfnArgs a, bool xf32, const float *wr, const float *bias, float *logits,
+                               hipStream_t stream) {
+  if (a.T != 1 || a.k > 8 || a.E > 16 * 64) return hipErrorNotSupported;
+  hipError_t err = launch_route_logits(a.x, !xf32, 1, a.D, a.E, wr, bias, logits, stream);
+  if (err != hipSuccess) return err;
+  a.u_max = a.k;
+  // row chunks as launch_gateup_gemv sets them (the same rows per block)
+  const int rpi = 64 / (a.D / 64);
+  a.rows_gu = min(a.F, 16 * rpi);
+  a.chunks_gu = (a.F + a.rows_gu - 1) / a.rows_gu;
+  a.rows_sg = min(a.F, 8 * rpi);
+  a.chunks_sg = a.sg ? (a.F + a.rows_sg - 1) / a.rows_sg : 0;
+  int32_t *ids_out = const_cast<int32_t *>(a.ids);
+  float *wts_out = const_cast<float *>(a.wts);
+  const dim3 grid(unsigned(a.chunks_sg + a.u_max * a.chunks_gu));
+  if (a.E <= 6 * 64) {
+    if (xf32)
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_sel_kernel<6, true>), grid, dim3(256), 0, stream, a, logits, ids_out,
+                wts_out);
+    else
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_sel_kernel<6, false>), grid, dim3(256), 0, stream, a, logits,
+                ids_out, wts_out);
+  } else {
+    if (xf32)
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_sel_kernel<16, true>), grid, dim3(256), 0, stream, a, logits,
+                ids_out, wts_out);
+    else
+      BM_LAUNCH("ffn_gateup_kernel", (ffn_gateup_sel_kernel<16, false>), grid, dim3(256), 0, stream, a, logits,
+                ids_out, wts_out);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_down_gemv<1, 1>(a, stream)) != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
                         stream);
 }

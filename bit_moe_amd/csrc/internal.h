@@ -88,6 +88,13 @@ struct FfnArgs {
   int u_max;
 };
 hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream);
+// router logits alone for T <= 8 tokens (the router_gemv_kernel launch of launch_route)
+hipError_t launch_route_logits(const void *x, bool xbf16, int T, int D, int E, const float *wr, const float *bias,
+                               float *logits, hipStream_t stream);
+// router + experts + combine of one token (T = 1) in four launches; a.ids and
+// a.wts receive the selection (hipErrorNotSupported for T != 1, k > 8, E > 1024)
+hipError_t launch_decode_layer(FfnArgs a, bool xf32, const float *wr, const float *bias, float *logits,
+                               hipStream_t stream);
 // int8 activation numerics (T <= 8; d_model, d_ff multiples of 256): a.hf /
 // a.hsf carry h, a.h* are unused
 hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream);
