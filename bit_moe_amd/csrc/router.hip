@@ -303,10 +303,9 @@ BM_DEVICE void topk_variant_token(const float *L, int E, int k, int score, const
                                   int32_t *ids, float *wts, int64_t *status, int64_t pair0, int lane) {
   float sc[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    sc[i] = e < E ? L[e] : -INFINITY;
-  }
+  for (int i = 0; i < PER; ++i) sc[i] = L[min(lane + 64 * i, E - 1)];  // every load issued before any use
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sc[i] = lane + 64 * i < E ? sc[i] : -INFINITY;
   if (score == 0) {  // softmax over the E logits
     float m = -INFINITY;
 #pragma unroll

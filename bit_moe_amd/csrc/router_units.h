@@ -83,36 +83,47 @@ BM_DEVICE float key_logit(uint32_t key) {
 }
 
 // Top-k of one token's logits by one wave; lane 0 writes ids and weights.
-// Round j: the wave-wide largest key M (DPP reduction); the selected expert is
-// the lowest index holding M (lowest slot i, then lowest lane, by ballot), so
-// an exact tie goes to the lower expert index.
+// Round j: every lane takes its largest remaining key and the lowest slot
+// holding it, the wave-wide largest key M comes from a DPP reduction, and the
+// selected expert is the lowest index e = lane + 64 slot among the lanes
+// holding M (one ballot; an exact tie across lanes is settled in a short
+// scalar loop), so an exact tie goes to the lower expert index.
 template <int PER>  // logits per lane: E <= 64 PER
 BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts, int lane) {
+  // all PER loads issued before any use (slots past E read logit E - 1 and
+  // are dropped), so their latencies overlap
+  float lv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) lv[i] = L[min(lane + 64 * i, E - 1)];
   uint32_t key[PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? logit_key(L[e]) : 0u;
-  }
+  for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? logit_key(lv[i]) : 0u;
   float sel_v[8];
   int sel_i[8];
   for (int j = 0; j < k; ++j) {
-    uint32_t m = 0;
+    uint32_t m = key[0];
+    int s = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) m = max(m, key[i]);
+    for (int i = 1; i < PER; ++i) {
+      const bool gt = key[i] > m;  // strictly: the lowest slot keeps an equal key
+      m = gt ? key[i] : m;
+      s = gt ? i : s;
+    }
     const uint32_t M = wave_max_u32(m);
     int bi = -1;  // only NaN logits left: no valid expert
     if (M != 0u) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const uint64_t hit = __ballot(key[i] == M);
-        if (hit) {
-          const int l = __builtin_ctzll(hit);
-          bi = l + 64 * i;
-          if (lane == l) key[i] = 0u;
-          break;
-        }
+      uint64_t hit = __ballot(m == M);
+      const int l = __builtin_ctzll(hit);
+      bi = l + 64 * __builtin_amdgcn_readlane(s, l);
+      hit &= hit - 1;
+      while (hit) {  // several lanes hold M: the lowest expert index among them
+        const int l2 = __builtin_ctzll(hit);
+        bi = min(bi, l2 + 64 * __builtin_amdgcn_readlane(s, l2));
+        hit &= hit - 1;
       }
+      const int wl = bi & 63, wsl = bi >> 6;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) key[i] = (lane == wl && i == wsl) ? 0u : key[i];
     }
     sel_v[j] = bi < 0 ? -INFINITY : key_logit(M);
     sel_i[j] = bi;
