@@ -804,36 +804,47 @@ __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ 
   const int t = int(idx / per_tok);
   const int c = int(idx % per_tok) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // the pair rows are loaded together with the ids (every row of y is in
-  // bounds; rows of skipped pairs are never used)
+  // every load is issued before any use, so their latencies overlap: the
+  // pair rows (all in bounds; rows of skipped pairs are never used), the ids,
+  // the weights and the shared expert's row
   float4 v[8];
+  int idv[8];
+  float wv[8];
+  const int64_t tk = int64_t(t) * k;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < k) v[j] = *reinterpret_cast<const float4 *>(y + (int64_t(t) * k + j) * D + c);
+  for (int j = 0; j < 8; ++j) {
+    const int jj = min(j, k - 1);
+    v[j] = *reinterpret_cast<const float4 *>(y + (tk + jj) * D + c);
+    idv[j] = ids[tk + jj];
+    wv[j] = wts[tk + jj];
+  }
+  const float4 vs = ys ? *reinterpret_cast<const float4 *>(ys + int64_t(t) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j >= k) break;
-    const int e = ids[t * k + j];
+    const int e = idv[j];
     if (e < 0 || e >= E) {
-      if (c == 0) record_fault(status, FAULT_BAD_EXPERT, int64_t(t) * k + j);
+      if (c == 0) record_fault(status, FAULT_BAD_EXPERT, tk + j);
       continue;
     }
-    if (repeats_earlier(ids + t * k, j, e)) {  // served once, at its first slot
-      if (c == 0) record_fault(status, FAULT_DUP_EXPERT, int64_t(t) * k + j);
+    bool dup = false;  // served once, at its first slot
+#pragma unroll
+    for (int i = 0; i < j; ++i) dup = dup || idv[i] == e;
+    if (dup) {
+      if (c == 0) record_fault(status, FAULT_DUP_EXPERT, tk + j);
       continue;
     }
-    const float w = wts[t * k + j];
+    const float w = wv[j];
     acc.x = __builtin_fmaf(w, v[j].x, acc.x);
     acc.y = __builtin_fmaf(w, v[j].y, acc.y);
     acc.z = __builtin_fmaf(w, v[j].z, acc.z);
     acc.w = __builtin_fmaf(w, v[j].w, acc.w);
   }
   if (ys) {
-    const float4 v = *reinterpret_cast<const float4 *>(ys + int64_t(t) * D + c);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    acc.x += vs.x;
+    acc.y += vs.y;
+    acc.z += vs.z;
+    acc.w += vs.w;
   }
   if (out_bf16) {
     uint2 o = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
