@@ -54,11 +54,18 @@ __global__ void __launch_bounds__(1024) plan_scan_kernel(int n_chunks, int E, in
   const int e = threadIdx.x;
   int32_t total = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      int32_t *cc = p.chunk_counts + int64_t(c) * E + e;
-      const int32_t v = *cc;
-      *cc = total;  // base of chunk c inside expert e's group
-      total += v;
+    // chunks in batches of 16: all of a batch's loads are issued before its
+    // stores, so their latencies overlap
+    for (int c0 = 0; c0 < n_chunks; c0 += 16) {
+      int32_t v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = p.chunk_counts[int64_t(min(c0 + i, n_chunks - 1)) * E + e];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i >= n_chunks) break;
+        p.chunk_counts[int64_t(c0 + i) * E + e] = total;  // base of chunk c inside expert e's group
+        total += v[i];
+      }
     }
   }
   s_cnt[e] = e < E ? total : 0;
@@ -106,21 +113,67 @@ __global__ void __launch_bounds__(64) plan_scatter_kernel(const int32_t *__restr
   const int chunk = blockIdx.x;
   const int t0 = chunk * 64;
   const int nt = min(64, T - t0);
-  for (int e = threadIdx.x; e < E; e += 64) s_pos[e] = p.offsets[e] + p.chunk_counts[int64_t(chunk) * E + e];
-  for (int i = threadIdx.x; i < nt * k; i += 64) s_ids[i] = ids[int64_t(t0) * k + i];
+  // every load of a batch is issued before its stores, so their latencies overlap
+  for (int e0 = 0; e0 < E; e0 += 64 * 8) {
+    int32_t o[8], c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = min(e0 + 64 * i + int(threadIdx.x), E - 1);
+      o[i] = p.offsets[e];
+      c[i] = p.chunk_counts[int64_t(chunk) * E + e];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = e0 + 64 * i + threadIdx.x;
+      if (e < E) s_pos[e] = o[i] + c[i];
+    }
+  }
+  for (int i0 = 0; i0 < nt * k; i0 += 64 * 8) {
+    int32_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = ids[int64_t(t0) * k + min(i0 + 64 * i + int(threadIdx.x), nt * k - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ii = i0 + 64 * i + threadIdx.x;
+      if (ii < nt * k) s_ids[ii] = v[i];
+    }
+  }
   __syncthreads();
-  // tokens of the chunk in order, lane j taking slot j: the pairs served are
-  // those of plan_count (in range, first slot of their expert in the token),
-  // so the k lanes of a step advance distinct counters and each expert's
-  // pairs land in token order (stable)
+  // which pairs are served (in range, first slot of their expert in the
+  // token), one token per thread; a pair that is not gets id -1
+  if (int(threadIdx.x) < nt) {
+    int32_t *row = s_ids + threadIdx.x * k;
+    int32_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = j < k ? row[j] : -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      bool keep = v[j] >= 0 && v[j] < E;
+#pragma unroll
+      for (int i = 0; i < j; ++i) keep = keep && v[i] != v[j];
+      if (!keep) row[j] = -1;
+    }
+  }
+  __syncthreads();
+  // tokens of the chunk in order, lane j taking slot j: the k lanes of a step
+  // advance distinct counters and each expert's pairs land in token order
+  // (stable).  The lane's ids are read ahead in groups of 16 tokens.
   const int j = threadIdx.x;
   if (j >= k) return;
-  for (int u = 0; u < nt; ++u) {
-    const int e = s_ids[u * k + j];
-    if (e < 0 || e >= E || repeats_earlier(s_ids + u * k, j, e)) continue;
-    const int pos = s_pos[e];
-    s_pos[e] = pos + 1;
-    p.perm[pos] = (t0 + u) * k + j;
+  for (int u0 = 0; u0 < nt; u0 += 16) {
+    int32_t ev[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ev[i] = s_ids[min(u0 + i, nt - 1) * k + j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = u0 + i, e = ev[i];
+      if (u >= nt) break;
+      if (e < 0) continue;
+      const int pos = s_pos[e];
+      s_pos[e] = pos + 1;
+      p.perm[pos] = (t0 + u) * k + j;
+    }
   }
 }
 
