@@ -122,7 +122,7 @@ struct PrefillArgs {
   uint16_t *hs_lo;
   uint16_t *sw_bf16;   // the shared expert expanded for its dense GEMMs (gate, up, down): 3 x F*D*17/8 bytes
   uint16_t *xsum;      // activation sub-block sums of the grouped GEMMs: max(T*D, T*k*F) / 8 bf16
-  float *xtot;         // activation super-block sums (float32): max(T*D, T*k*F) / 256
+  float *xtot;         // -128 x the activation super-block sums (float32): max(T*D, T*k*F) / 256
   float *y;            // [T*k][D] float32, pair order
   float *ys;           // [T][D]
   void *out;

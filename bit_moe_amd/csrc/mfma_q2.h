@@ -78,8 +78,8 @@ BM_DEVICE void q2_min_operand(const Q2Raw &r, int p, uint32_t (&B)[4]) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const uint32_t scw = (s < 2 ? r.sc.x : r.sc.y) >> (8 * p + 16 * (s & 1));
-    const uint32_t m = bf16_of_small((scw >> 4) & 0xFu);
-    B[s] = m | (m << 16);
+    const uint32_t f = __float_as_uint(float((scw >> 4) & 0xFu));  // m, exact
+    B[s] = __builtin_amdgcn_perm(f, f, 0x03020302u);               // its bf16 bits (the high half) twice
   }
 }
 

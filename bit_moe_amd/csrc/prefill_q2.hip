@@ -54,7 +54,7 @@ constexpr int MT_DN = BM_PF_CHUNK_DN;  // down: M-tiles of 16 pairs per chunk (h
 // ---- activation sub-block sums --------------------------------------------
 // out[row][kb][slot]: the 16 sub-block sums of columns [256 kb, 256 kb + 256)
 // of row `row` (over both parts when a_lo is given), each split into bf16 hi +
-// lo and placed at q2_sum_slot(sub-block, part); tot[row][kb]: their float32
+// lo and placed at q2_sum_slot(sub-block, part); tot[row][kb]: -128 times their float32
 // total.  One thread per sub-block; the 16 threads of a super-block are 16
 // consecutive lanes of one wave.
 __global__ void __launch_bounds__(256) xsum_kernel(const uint16_t *__restrict__ a, const uint16_t *__restrict__ a_lo,
@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(256) xsum_kernel(const uint16_t *__restrict__ 
   float t = sum;
 #pragma unroll
   for (int m = 8; m > 0; m >>= 1) t += __shfl_xor(t, m, 16);
-  if (sb == 0) tot[row * (K / KS) + kb] = t;
+  if (sb == 0) tot[row * (K / KS) + kb] = -128.f * t;  // exact: a power of two
 }
 
 // ---- grouped GEMM ---------------------------------------------------------------
@@ -273,7 +273,7 @@ BM_DEVICE void group_body(const GroupArgs &g, int e, int valid, int base, int nt
     for (int mi = 0; mi < NT; ++mi) {
       ld16(Sx + (16 * mi + nl) * SUMS + 8 * gq, As[mi]);
       const float4 xt = *reinterpret_cast<const float4 *>(Xt + 16 * mi + 4 * gq);
-      const f32x4_t cx = {-128.f * xt.x, -128.f * xt.y, -128.f * xt.z, -128.f * xt.w};
+      const f32x4_t cx = {xt.x, xt.y, xt.z, xt.w};
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
