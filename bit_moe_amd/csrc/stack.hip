@@ -15,66 +15,56 @@
 
 namespace bm {
 
-// Thread i of the block owns the 16 consecutive elements 16 i .. 16 i + 15 of
-// the row (D / 16 <= 256 threads busy): 16-byte loads and stores.
+// Thread i of the block owns the 4 consecutive elements 4 i .. 4 i + 3 of the
+// row (D / 4 <= 1024 threads busy): sixteen waves share the float64 divisions
+// of the row, so their latencies overlap.
 template <bool Y_F32>
-__global__ void __launch_bounds__(256) residual_rescale_kernel(const uint16_t *__restrict__ x, const void *__restrict__ y,
-                                                               int D, uint16_t *__restrict__ out) {
-  __shared__ double part[4];
+__global__ void __launch_bounds__(1024) residual_rescale_kernel(const uint16_t *__restrict__ x, const void *__restrict__ y,
+                                                                int D, uint16_t *__restrict__ out) {
+  __shared__ double part[16];
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = size_t(t) * D;
-  const bool busy = 16 * tid < D;
-  double r[16];
+  const bool busy = 4 * tid < D;
+  double r[4];
   double ss = 0.0;
   if (busy) {
-    const size_t c = row + 16 * size_t(tid);
-    const uint4 xa = reinterpret_cast<const uint4 *>(x + c)[0], xb = reinterpret_cast<const uint4 *>(x + c)[1];
-    const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    float yv[16];
+    const size_t c = row + 4 * size_t(tid);
+    const uint2 xw = *reinterpret_cast<const uint2 *>(x + c);
+    float yv[4];
     if constexpr (Y_F32) {
-      const float4 *yp = reinterpret_cast<const float4 *>(static_cast<const float *>(y) + c);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = yp[q];
-        yv[4 * q] = v.x, yv[4 * q + 1] = v.y, yv[4 * q + 2] = v.z, yv[4 * q + 3] = v.w;
-      }
+      const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(y) + c);
+      yv[0] = v.x, yv[1] = v.y, yv[2] = v.z, yv[3] = v.w;
     } else {
-      const uint4 *yp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(y) + c);
-      const uint4 ya = yp[0], yb = yp[1];
-      const uint32_t yw[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) yv[2 * q] = bf16_lo(yw[q]), yv[2 * q + 1] = bf16_hi(yw[q]);
+      const uint2 yw = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(y) + c);
+      yv[0] = bf16_lo(yw.x), yv[1] = bf16_hi(yw.x), yv[2] = bf16_lo(yw.y), yv[3] = bf16_hi(yw.y);
     }
+    r[0] = double(bf16_lo(xw.x)) + double(yv[0]);
+    r[1] = double(bf16_hi(xw.x)) + double(yv[1]);
+    r[2] = double(bf16_lo(xw.y)) + double(yv[2]);
+    r[3] = double(bf16_hi(xw.y)) + double(yv[3]);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      r[2 * q] = double(bf16_lo(xw[q])) + double(yv[2 * q]);
-      r[2 * q + 1] = double(bf16_hi(xw[q])) + double(yv[2 * q + 1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ss = fma(r[i], r[i], ss);
+    for (int i = 0; i < 4; ++i) ss = fma(r[i], r[i], ss);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if (lane == 0) part[wave] = ss;
   __syncthreads();
   if (!busy) return;
-  const double total = (part[0] + part[1]) + (part[2] + part[3]);
-  const double rms = sqrt(total / D + 1e-6);
-  uint32_t o[8];
+  double total = 0.0;
 #pragma unroll
-  for (int q = 0; q < 8; ++q)
-    o[q] = uint32_t(bf16_from_f64(r[2 * q] / rms)) | (uint32_t(bf16_from_f64(r[2 * q + 1] / rms)) << 16);
-  uint4 *op = reinterpret_cast<uint4 *>(out + row + 16 * size_t(tid));
-  op[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  op[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int w = 0; w < 16; ++w) total += part[w];
+  const double rms = sqrt(total / D + 1e-6);
+  const uint32_t o0 = uint32_t(bf16_from_f64(r[0] / rms)) | (uint32_t(bf16_from_f64(r[1] / rms)) << 16);
+  const uint32_t o1 = uint32_t(bf16_from_f64(r[2] / rms)) | (uint32_t(bf16_from_f64(r[3] / rms)) << 16);
+  *reinterpret_cast<uint2 *>(out + row + 4 * size_t(tid)) = make_uint2(o0, o1);
 }
 
 hipError_t launch_residual_rescale(const uint16_t *x, const void *y, bool y_f32, int T, int D, uint16_t *out,
                                    hipStream_t stream) {
   if (y_f32)
-    BM_LAUNCH("residual_rescale_kernel", residual_rescale_kernel<true>, dim3(T), dim3(256), 0, stream, x, y, D, out);
+    BM_LAUNCH("residual_rescale_kernel", residual_rescale_kernel<true>, dim3(T), dim3(1024), 0, stream, x, y, D, out);
   else
-    BM_LAUNCH("residual_rescale_kernel", residual_rescale_kernel<false>, dim3(T), dim3(256), 0, stream, x, y, D, out);
+    BM_LAUNCH("residual_rescale_kernel", residual_rescale_kernel<false>, dim3(T), dim3(1024), 0, stream, x, y, D, out);
   return hipGetLastError();
 }
 
