@@ -501,8 +501,9 @@ def bench_engram_inject(bm, torch, np, synthdata, args, lut, dev) -> dict:
 
 def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
     """40-layer resident stack: decode T=1 and T=5 (HIP graph) and a prefill
-    chunk of T=8192 (eager), each step running every layer (route, experts +
-    combine, Engram at layers 1 and 14, residual step)."""
+    chunk of T=8192 (eager), each step running every layer (Engram gather at
+    layers 1 and 14, then moe_layer_residual: route, experts, and the combine
+    fused with the residual step into the next layer's input)."""
     cfg = synthdata.CONFIGS["stack"]
     t0 = time.time()
     layers = [make_layer(bm, torch, synthdata, cfg, args.seed, l, lut, dev)[0] for l in range(cfg.n_layers)]
@@ -537,11 +538,12 @@ def bench_stack(bm, torch, np, synthdata, args, lut, dev) -> dict:
         def step(i):
             x = xs[i]
             for l, L in enumerate(layers):
-                bm.layer(L, x, ws, ids=ids, weights=wts, y=y, mode=mode)
                 if l in tables:
                     t, j = tables[l]
                     bm.engram_gather(t, rid[i][j], out=rows)
-                x = bm.residual_rescale(x, y, out=xb[l & 1])
+                # the layer, its combine fused with the residual step into the next input
+                bm.layer(L, x, ws, ids=ids, weights=wts, y=y, mode=mode, x_next=xb[l & 1])
+                x = xb[l & 1]
 
         graph_ms, eager_ms, prof = time_steps(bm, torch, step, K, W, graph)
         step_ms = (graph_ms if graph_ms is not None else eager_ms) / K

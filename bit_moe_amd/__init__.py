@@ -34,7 +34,7 @@ EXPORTS = [
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
     "bitmoe_residual_rescale", "engram_inject", "engram_inject_workspace_size", "moe_route_noalloc",
-    "bitmoe_probe_mfma", "moe_layer",
+    "bitmoe_probe_mfma", "moe_layer", "moe_layer_residual",
 ]
 
 
@@ -82,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_route_ex": [LP, P, I32, I32, ctypes.POINTER(_RouteOptsC), P, P, P, SZ, P],
         "moe_expert_ffn": [LP, P, I32, I32, P, P, P, I32, I32, P, SZ, P],
         "moe_layer": [LP, P, I32, I32, P, P, P, P, I32, I32, P, SZ, P],
+        "moe_layer_residual": [LP, P, I32, P, P, P, P, I32, P, I32, P, SZ, P],
         "engram_gather": [P, I64, P, I64, P, P, P],
         "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "bitmoe_plan_workspace_size": [I32, I32, I32, ctypes.POINTER(SZ)],
@@ -280,9 +281,12 @@ def expert_ffn(layer: Layer, x: torch.Tensor, ids: torch.Tensor, weights: torch.
 
 def layer(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.Tensor] = None,
           ids: Optional[torch.Tensor] = None, weights: Optional[torch.Tensor] = None,
-          y: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16, mode: int = MODE_AUTO, stream=None):
+          y: Optional[torch.Tensor] = None, out_dtype=torch.bfloat16, mode: int = MODE_AUTO, stream=None,
+          x_next: Optional[torch.Tensor] = None):
     """moe_layer: moe_route followed by moe_expert_ffn in one call (one token in
-    decode mode runs in four launches).  Returns (ids, weights, y)."""
+    decode mode runs in four launches).  Returns (ids, weights, y).  With
+    x_next (bf16 [T][d_model], x bf16): moe_layer_residual, which also writes
+    the stack's residual step of x and y into x_next from the combine launch."""
     lib = load()
     _require(x, "x")
     T = x.shape[0]
@@ -298,6 +302,12 @@ def layer(layer: Layer, x: torch.Tensor, ws: torch.Tensor, bias: Optional[torch.
     if bias is not None:
         _require(bias, "bias", torch.float32)
     lc = layer.c()
+    if x_next is not None:
+        _require(x, "x", torch.bfloat16)
+        _require(x_next, "x_next", torch.bfloat16)
+        _check(lib.moe_layer_residual(ctypes.byref(lc), _ptr(x), T, _ptr(bias), _ptr(ids), _ptr(weights), _ptr(y),
+                                      _dtype_code(y), _ptr(x_next), mode, _ptr(ws), ws.numel(), _stream(stream)))
+        return ids, weights, y
     _check(lib.moe_layer(ctypes.byref(lc), _ptr(x), _dtype_code(x), T, _ptr(bias), _ptr(ids), _ptr(weights),
                          _ptr(y), _dtype_code(y), mode, _ptr(ws), ws.numel(), _stream(stream)))
     return ids, weights, y

@@ -420,10 +420,12 @@ int moe_route_ex(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t 
   return BITMOE_OK;
 }
 
-int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const int32_t *topk_ids,
-                   const float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
-                   hipStream_t stream) {
-  const char *fn = "moe_expert_ffn";
+// moe_expert_ffn; with x_next set (x bf16, checked by the caller) the combine
+// launch also runs the stack's residual step into x_next.
+static int expert_ffn_impl(const char *fn, const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T,
+                           const int32_t *topk_ids, const float *topk_w, void *y, int32_t y_dtype, int32_t mode,
+                           void *ws, size_t ws_bytes, uint16_t *x_next, hipStream_t stream) {
+  const uint16_t *x_res = x_next ? static_cast<const uint16_t *>(x) : nullptr;
   int rc = check_layer(fn, L);
   if (rc) return rc;
   if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
@@ -448,13 +450,17 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   carve_common(c, L, T, &status, nullptr);
   const bool shared = L->shared_wfmt == BITMOE_WFMT_Q8_0;
   if (m == BITMOE_MODE_DECODE) {
-    const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
+    bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
+    a.x_res = x_res;
+    a.x_next = x_next;
     hipError_t e = bm::launch_decode_ffn(a, x_dtype == BITMOE_F32, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
     return BITMOE_OK;
   }
   if (m == BITMOE_MODE_DECODE_INT8) {
-    const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status, true);
+    bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status, true);
+    a.x_res = x_res;
+    a.x_next = x_next;
     hipError_t e = bm::launch_decode_ffn_i8(a, x_dtype == BITMOE_F32, stream);
     if (e != hipSuccess) return hip_fail(fn, e);
     return BITMOE_OK;
@@ -481,6 +487,8 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
     a.out = y;
     a.out_bf16 = y_dtype == BITMOE_BF16;
     a.status = status;
+    a.x_res = x_res;
+    a.x_next = x_next;
     hipError_t e = bm::launch_prefill_ffn_i8(a, stream);
     if (e == hipErrorNotSupported)
       return fail(BITMOE_EUNSUPPORTED, "%s: int8 prefill path not available for this shape", fn);
@@ -522,16 +530,24 @@ int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_
   a.out = y;
   a.out_bf16 = y_dtype == BITMOE_BF16;
   a.status = status;
+  a.x_res = x_res;
+  a.x_next = x_next;
   hipError_t e = bm::launch_prefill_ffn(a, stream);
   if (e == hipErrorNotSupported) return fail(BITMOE_EUNSUPPORTED, "%s: prefill path not available for this shape", fn);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }
 
-int moe_layer(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const float *logit_bias,
-              int32_t *topk_ids, float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
-              hipStream_t stream) {
-  const char *fn = "moe_layer";
+int moe_expert_ffn(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const int32_t *topk_ids,
+                   const float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  return expert_ffn_impl("moe_expert_ffn", L, x, x_dtype, T, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes,
+                         nullptr, stream);
+}
+
+static int layer_impl(const char *fn, const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T,
+                      const float *logit_bias, int32_t *topk_ids, float *topk_w, void *y, int32_t y_dtype, int32_t mode,
+                      void *ws, size_t ws_bytes, uint16_t *x_next, hipStream_t stream) {
   int rc = check_layer(fn, L);
   if (rc) return rc;
   if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
@@ -541,7 +557,7 @@ int moe_layer(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, 
     // the two calls' launches in order
     rc = moe_route(L, x, x_dtype, T, logit_bias, topk_ids, topk_w, ws, ws_bytes, stream);
     if (rc) return rc;
-    return moe_expert_ffn(L, x, x_dtype, T, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes, stream);
+    return expert_ffn_impl(fn, L, x, x_dtype, T, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes, x_next, stream);
   }
   if (x_dtype != BITMOE_F32 && x_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
   if (y_dtype != BITMOE_F32 && y_dtype != BITMOE_BF16) return fail(BITMOE_EUNSUPPORTED, "%s: y_dtype %d", fn, y_dtype);
@@ -556,10 +572,36 @@ int moe_layer(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, 
   int64_t *status;
   float *logits;
   carve_common(c, L, T, &status, &logits);
-  const bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
+  bm::FfnArgs a = decode_args(c, L, x, T, topk_ids, topk_w, y, y_dtype, status);
+  a.x_res = x_next ? static_cast<const uint16_t *>(x) : nullptr;
+  a.x_next = x_next;
   hipError_t e = bm::launch_decode_layer(a, x_dtype == BITMOE_F32, L->w_router, logit_bias, logits, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
+}
+
+int moe_layer(const bitmoe_layer *L, const void *x, int32_t x_dtype, int32_t T, const float *logit_bias,
+              int32_t *topk_ids, float *topk_w, void *y, int32_t y_dtype, int32_t mode, void *ws, size_t ws_bytes,
+              hipStream_t stream) {
+  return layer_impl("moe_layer", L, x, x_dtype, T, logit_bias, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes,
+                    nullptr, stream);
+}
+
+int moe_layer_residual(const bitmoe_layer *L, const void *x, int32_t T, const float *logit_bias, int32_t *topk_ids,
+                       float *topk_w, void *y, int32_t y_dtype, void *x_next, int32_t mode, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  const char *fn = "moe_layer_residual";
+  int rc = check_layer(fn, L);
+  if (rc) return rc;
+  if (L->d_model % 16 || L->d_model > 4096)
+    return fail(BITMOE_EUNSUPPORTED, "%s: the residual step takes d_model a multiple of 16 up to 4096, got %d", fn,
+                L->d_model);
+  if (T < 0) return fail(BITMOE_EINVAL, "%s: T=%d is negative", fn, T);
+  if (T == 0) return BITMOE_OK;
+  if (!x_next || !aligned(x_next, 16)) return fail(BITMOE_EINVAL, "%s: x_next is NULL or not 16-byte aligned", fn);
+  if (x_next == y) return fail(BITMOE_EINVAL, "%s: x_next must not alias y", fn);
+  return layer_impl(fn, L, x, BITMOE_BF16, T, logit_bias, topk_ids, topk_w, y, y_dtype, mode, ws, ws_bytes,
+                    static_cast<uint16_t *>(x_next), stream);
 }
 
 int engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n, uint16_t *out,

@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "combine_units.h"
 #include "decode_job.h"
 #include "gemv_units.h"
 #include "router_units.h"
@@ -794,64 +795,17 @@ static hipError_t launch_stream(FfnArgs a, int rows_r, int rows_s, hipStream_t s
 // ---- combine ----------------------------------------------------------------
 // y is indexed by pair; pairs whose id is out of range contribute nothing.
 
+template <int K>
 __global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ y, const float *__restrict__ ys,
                                                       const int32_t *__restrict__ ids,
-                                                      const float *__restrict__ wts, int T, int k, int D, int E,
+                                                      const float *__restrict__ wts, int T, int D, int E,
                                                       void *out, int out_bf16, int64_t *status) {
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // one thread per 4 outputs
   const int64_t per_tok = D / 4;
   if (idx >= int64_t(T) * per_tok) return;
   const int t = int(idx / per_tok);
   const int c = int(idx % per_tok) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // every load is issued before any use, so their latencies overlap: the
-  // pair rows (all in bounds; rows of skipped pairs are never used), the ids,
-  // the weights and the shared expert's row
-  float4 v[8];
-  int idv[8];
-  float wv[8];
-  const int64_t tk = int64_t(t) * k;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int jj = min(j, k - 1);
-    v[j] = *reinterpret_cast<const float4 *>(y + (tk + jj) * D + c);
-    idv[j] = ids[tk + jj];
-    wv[j] = wts[tk + jj];
-  }
-  const float4 vs = ys ? *reinterpret_cast<const float4 *>(ys + int64_t(t) * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    const int e = idv[j];
-    if (e < 0 || e >= E) {
-      if (c == 0) record_fault(status, FAULT_BAD_EXPERT, tk + j);
-      continue;
-    }
-    bool dup = false;  // served once, at its first slot
-#pragma unroll
-    for (int i = 0; i < j; ++i) dup = dup || idv[i] == e;
-    if (dup) {
-      if (c == 0) record_fault(status, FAULT_DUP_EXPERT, tk + j);
-      continue;
-    }
-    const float w = wv[j];
-    acc.x = __builtin_fmaf(w, v[j].x, acc.x);
-    acc.y = __builtin_fmaf(w, v[j].y, acc.y);
-    acc.z = __builtin_fmaf(w, v[j].z, acc.z);
-    acc.w = __builtin_fmaf(w, v[j].w, acc.w);
-  }
-  if (ys) {
-    acc.x += vs.x;
-    acc.y += vs.y;
-    acc.z += vs.z;
-    acc.w += vs.w;
-  }
-  if (out_bf16) {
-    uint2 o = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + int64_t(t) * D + c) = o;
-  } else {
-    *reinterpret_cast<float4 *>(static_cast<float *>(out) + int64_t(t) * D + c) = acc;
-  }
+  store_out4(out, out_bf16, t, D, c, combine4<K>(y, ys, ids, wts, t, c, D, E, status));
 }
 
 // ---- launch -----------------------------------------------------------------
@@ -896,7 +850,7 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
     err = launch_decode_nt<NTOK, 2, 2, false>(a, stream);
   if (err != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
-                        stream);
+                        a.x_res, a.x_next, stream);
 }
 
 // ---- one decode step of one token in four launches ---------------------------
@@ -977,15 +931,19 @@ hipError_t launch_decode_layer(FfnArgs a, bool xf32, const float *wr, const floa
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if ((err = launch_down_gemv<1, 1>(a, stream)) != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
-                        stream);
+                        a.x_res, a.x_next, stream);
 }
 
 hipError_t launch_combine(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k, int D,
-                          int E, void *out, int out_bf16, int64_t *status, hipStream_t stream) {
+                          int E, void *out, int out_bf16, int64_t *status, const uint16_t *x_res, uint16_t *x_next,
+                          hipStream_t stream) {
+  if (x_next) return launch_combine_residual(y, ys, ids, wts, T, k, D, E, out, out_bf16, status, x_res, x_next, stream);
   const int64_t n4 = int64_t(T) * (D / 4);
-  BM_LAUNCH("combine_kernel", combine_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, stream, y, ys, ids, wts,
-            T, k, D, E, out, out_bf16, status);
-  return hipGetLastError();
+  return with_top_k(k, [&](auto kc) {
+    BM_LAUNCH("combine_kernel", combine_kernel<decltype(kc)::value>, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
+              stream, y, ys, ids, wts, T, D, E, out, out_bf16, status);
+    return hipGetLastError();
+  });
 }
 
 }  // namespace bm

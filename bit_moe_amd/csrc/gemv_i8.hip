@@ -502,7 +502,7 @@ hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream) {
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_combine(a.y, a.sd ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
-                        stream);
+                        a.x_res, a.x_next, stream);
 }
 
 hipError_t launch_quantize_q8(const void *x, bool xf32, int64_t rows, int cols, uint8_t *q, float *d, float *s,

@@ -81,6 +81,8 @@ struct FfnArgs {
   void *out;
   int out_bf16;
   int64_t *status;
+  const uint16_t *x_res;  // with x_next: the combine also runs the residual step of x_res (bf16)
+  uint16_t *x_next;
   int chunks_gu, rows_gu;   // routed gate/up: row chunks per job, rows per chunk
   int chunks_dn, rows_dn;   // routed down
   int chunks_sg, rows_sg;   // shared gate/up (0 chunks: no shared blocks in the launch)
@@ -101,8 +103,15 @@ hipError_t launch_decode_ffn_i8(FfnArgs a, bool xf32, hipStream_t stream);
 // the int8 mode's quantiser over [rows][cols] (cols a multiple of 32)
 hipError_t launch_quantize_q8(const void *x, bool xf32, int64_t rows, int cols, uint8_t *q, float *d, float *s,
                               hipStream_t stream);
+// The combine of every path (out = the layer output); with x_next set, the
+// same launch also runs the stack's residual step x_next = rescale(x_res + out)
+// (x_res bf16 [T][D], D a multiple of 16 up to 4096; stack.hip).
 hipError_t launch_combine(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k, int D,
-                          int E, void *out, int out_bf16, int64_t *status, hipStream_t stream);
+                          int E, void *out, int out_bf16, int64_t *status, const uint16_t *x_res, uint16_t *x_next,
+                          hipStream_t stream);
+hipError_t launch_combine_residual(const float *y, const float *ys, const int32_t *ids, const float *wts, int T, int k,
+                                   int D, int E, void *out, int out_bf16, int64_t *status, const uint16_t *x,
+                                   uint16_t *x_next, hipStream_t stream);
 
 struct PrefillArgs {
   int D, F, E, k, T;
@@ -128,6 +137,8 @@ struct PrefillArgs {
   void *out;
   int out_bf16;
   int64_t *status;
+  const uint16_t *x_res;  // with x_next: the combine also runs the residual step of x_res (bf16)
+  uint16_t *x_next;
 };
 hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream);
 // routed grouped GEMM (gate/up with h out, or down with y out) over the plan's
@@ -159,6 +170,8 @@ struct PrefillI8Args {
   void *out;
   int out_bf16;
   int64_t *status;
+  const uint16_t *x_res;  // with x_next: the combine also runs the residual step of x_res (bf16)
+  uint16_t *x_next;
 };
 hipError_t launch_prefill_ffn_i8(const PrefillI8Args &a, hipStream_t stream);
 hipError_t launch_probe_mfma(int blocks, int iters, uint32_t *sink, hipStream_t stream);

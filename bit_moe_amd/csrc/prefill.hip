@@ -282,7 +282,7 @@ hipError_t launch_prefill_ffn(const PrefillArgs &a, hipStream_t stream) {
     if ((err = launch_q8_dense<false>(s, stream)) != hipSuccess) return err;
   }
   return launch_combine(a.y, a.sg ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
-                        stream);
+                        a.x_res, a.x_next, stream);
 }
 
 }  // namespace bm

@@ -610,7 +610,7 @@ hipError_t launch_prefill_ffn_i8(const PrefillI8Args &a, hipStream_t stream) {
     if ((err = launch_dense_i8(false, s, stream)) != hipSuccess) return err;
   }
   return launch_combine(a.y, a.sg ? a.ys : nullptr, a.ids, a.wts, a.T, a.k, a.D, a.E, a.out, a.out_bf16, a.status,
-                        stream);
+                        a.x_res, a.x_next, stream);
 }
 
 }  // namespace bm

@@ -156,6 +156,21 @@ def test_expert_ffn_rejects_bad_args(lib):
     assert lib.moe_expert_ffn(*args(T=0, x=None, y=None)) == bm.OK
 
 
+def test_layer_residual_rejects_bad_args(lib):
+    # moe_layer_residual checks the layer, x_next and its aliasing before
+    # anything reaches moe_layer's launches
+    P = ctypes.c_void_p
+    args = lambda L=None, **k: [ctypes.byref(L or _layer()), P(0x10000), k.get("T", 1), None, P(0x10000),
+                                P(0x10000), k.get("y", P(0x20000)), bm.BF16, k.get("xn", P(0x30000)), bm.MODE_AUTO,
+                                P(0x10000), 1 << 40, None]
+    assert lib.moe_layer_residual(*args(xn=None)) == bm.EINVAL
+    assert lib.moe_layer_residual(*args(xn=P(0x30008))) == bm.EINVAL  # not 16-byte aligned
+    assert lib.moe_layer_residual(*args(xn=P(0x20000))) == bm.EINVAL  # aliases y
+    assert lib.moe_layer_residual(*args(L=_layer(top_k=400))) == bm.EINVAL
+    assert lib.moe_layer_residual(*args(T=-1)) == bm.EINVAL
+    assert lib.moe_layer_residual(*args(T=0, xn=None)) == bm.OK
+
+
 def test_int8_mode_workspace_and_shape_limits(lib):
     L = _layer()
     n8, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -92,6 +92,19 @@ def test_stack_sampled_layers(stack, T):
         x = xn
     torch.cuda.synchronize()
     print(f"[stack] T={T}: {cfg.n_layers} layers run")
+    # the same stack through moe_layer_residual (combine + residual step in one
+    # launch, as the bench runs it): every layer's output and the final
+    # hidden state bit for bit
+    xf = torch.from_numpy(synthdata.activations_bf16(1, 40 + T, T, cfg.d_model).view(np.int16)).cuda()
+    xf = xf.view(torch.bfloat16)
+    for l in range(cfg.n_layers):
+        xn = torch.empty_like(xf)
+        _, _, y = bm.layer(layers[l], xf, ws, x_next=xn)
+        if l in SAMPLED:
+            assert np.array_equal(_bits(y), _bits(saved[l][2])), l
+            assert np.array_equal(_bits(xn), _bits(saved[l][3])), l
+        xf = xn
+    assert np.array_equal(_bits(xf), _bits(x))
     for l in SAMPLED:
         xin, ids, y, xn = saved[l]
         xv = formats.bf16_to_f64(_bits(xin))
