@@ -819,11 +819,12 @@ static hipError_t launch_decode_nt(const FfnArgs &a, hipStream_t stream) {
 }
 
 // Streamed gate/up (K = D) and down (K = F) with NT_S / NT_R token passes.
-template <int D, int F, int NT_S, int NT_R, bool XF32>
+// NT_SG / NT_SD: tokens per pass of the shared expert's gate/up / down rows
+template <int D, int F, int NT_SG, int NT_SD, int NT_R, bool XF32>
 static hipError_t launch_stream_ffn(const FfnArgs &a, hipStream_t stream) {
-  hipError_t err = launch_stream<D, NT_S, NT_R, true, XF32>(a, STREAM_ROWS_GU, STREAM_ROWS_SG, stream);
+  hipError_t err = launch_stream<D, NT_SG, NT_R, true, XF32>(a, STREAM_ROWS_GU, STREAM_ROWS_SG, stream);
   if (err != hipSuccess) return err;
-  return launch_stream<F, NT_S, NT_R, false, XF32>(a, STREAM_ROWS_DN, STREAM_ROWS_SD, stream);
+  return launch_stream<F, NT_SD, NT_R, false, XF32>(a, STREAM_ROWS_DN, STREAM_ROWS_SD, stream);
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -842,8 +843,12 @@ hipError_t launch_decode_ffn(FfnArgs a, bool xf32, hipStream_t stream) {
   if (a.T == 1)
     err = xf32 ? launch_decode_nt<1, 1, 1, true>(a, stream) : launch_decode_nt<1, 1, 1, false>(a, stream);
   else if (stream_ok)
-    err = xf32 ? launch_stream_ffn<4096, 2048, 2, 2, true>(a, stream)
-               : launch_stream_ffn<4096, 2048, 2, 2, false>(a, stream);
+    // bf16 x from three tokens on: the shared gate/up rows in passes of three
+    // (two passes at T = 5 instead of three; 156 VGPRs against 146, the same
+    // three waves per SIMD); down keeps passes of two (three would take 256)
+    err = xf32 ? launch_stream_ffn<4096, 2048, 2, 2, 2, true>(a, stream)
+               : (a.T == 2 ? launch_stream_ffn<4096, 2048, 2, 2, 2, false>(a, stream)
+                           : launch_stream_ffn<4096, 2048, 3, 2, 2, false>(a, stream));
   else if (a.T == 2 || xf32)
     err = xf32 ? launch_decode_nt<2, 2, 2, true>(a, stream) : launch_decode_nt<2, 2, 2, false>(a, stream);
   else
