@@ -29,7 +29,7 @@ SCORE_SOFTMAX, SCORE_SQRT_SOFTPLUS = 0, 1
 FILL_RAW, FILL_Q2, FILL_Q8, FILL_ENGRAM = 0, 1, 2, 3
 
 EXPORTS = [
-    "bitmoe_workspace_size", "moe_route", "moe_route_ex", "moe_expert_ffn", "engram_gather", "moe_plan",
+    "bitmoe_workspace_size", "moe_route", "moe_route_ex", "moe_expert_ffn", "engram_gather", "engram_gather_tables", "moe_plan",
     "bitmoe_plan_workspace_size", "moe_dequant", "moe_quantize_q8_1", "bitmoe_fill", "bitmoe_read_status",
     "bitmoe_ws_status", "bitmoe_strerror", "bitmoe_last_error",
     "bitmoe_profile_start", "bitmoe_profile_stop", "bitmoe_profile_get", "bitmoe_probe_read",
@@ -84,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_layer": [LP, P, I32, I32, P, P, P, P, I32, I32, P, SZ, P],
         "moe_layer_residual": [LP, P, I32, P, P, P, P, I32, P, I32, P, SZ, P],
         "engram_gather": [P, I64, P, I64, P, P, P],
+        "engram_gather_tables": [P, P, I32, P, I64, I32, P, P, P],
         "moe_plan": [P, I32, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "bitmoe_plan_workspace_size": [I32, I32, I32, ctypes.POINTER(SZ)],
         "moe_dequant": [P, I32, I64, P, I32, P],
@@ -356,6 +357,29 @@ def engram_gather(table: torch.Tensor, row_ids: torch.Tensor, out: Optional[torc
         _require(status, "status", torch.int64)
     _check(lib.engram_gather(_ptr(table), table.numel() // 264, _ptr(row_ids), n, _ptr(out), _ptr(status),
                              _stream(stream)))
+    return out
+
+
+def engram_gather_tables(tables, row_ids: torch.Tensor, out: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """tables: list of [n_rows][264] uint8 tables; row_ids int64 [n_groups][n_tables][per]
+    -> bf16 bits as int16 [n_groups][n_tables][per][256], one launch for every table."""
+    lib = load()
+    nt = len(tables)
+    for j, t in enumerate(tables):
+        _require(t, f"tables[{j}]", torch.uint8)
+    _require(row_ids, "row_ids", torch.int64)
+    if row_ids.dim() != 3 or row_ids.shape[1] != nt:
+        raise ValueError(f"row_ids must be [n_groups][{nt}][per], got {tuple(row_ids.shape)}")
+    if out is None:
+        out = torch.empty(tuple(row_ids.shape) + (256,), dtype=torch.int16, device=row_ids.device)
+    _require(out, "out")
+    if status is not None:
+        _require(status, "status", torch.int64)
+    ptrs = (ctypes.c_void_p * nt)(*[t.data_ptr() for t in tables])
+    rows = (ctypes.c_int64 * nt)(*[t.numel() // 264 for t in tables])
+    _check(lib.engram_gather_tables(ptrs, rows, nt, _ptr(row_ids), row_ids.shape[0], row_ids.shape[2], _ptr(out),
+                                    _ptr(status), _stream(stream)))
     return out
 
 

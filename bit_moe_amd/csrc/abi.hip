@@ -615,7 +615,41 @@ int engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, 
   if (!out || !aligned(out, 16)) return fail(BITMOE_EINVAL, "%s: out is NULL or not 16-byte aligned", fn);
   if (status && !aligned(status, 8)) return fail(BITMOE_EINVAL, "%s: status not 8-byte aligned", fn);
   if (n > (int64_t(1) << 33)) return fail(BITMOE_EUNSUPPORTED, "%s: n=%lld rows in one call", fn, (long long)n);
-  hipError_t e = bm::launch_engram_gather(table, n_rows, row_ids, n, out, status, stream);
+  bm::EngramTables tabs{};
+  tabs.table[0] = table;
+  tabs.rows[0] = n_rows;
+  tabs.n = 1;
+  hipError_t e = bm::launch_engram_gather(tabs, int32_t(1), row_ids, n, out, status, stream);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return BITMOE_OK;
+}
+
+int engram_gather_tables(const uint8_t *const *tables, const int64_t *n_rows, int32_t n_tables,
+                         const int64_t *row_ids, int64_t n_groups, int32_t per, uint16_t *out, int64_t *status,
+                         hipStream_t stream) {
+  const char *fn = "engram_gather_tables";
+  if (n_tables < 1 || n_tables > bm::ENGRAM_MAX_TABLES)
+    return fail(BITMOE_EINVAL, "%s: n_tables=%d outside 1..%d", fn, n_tables, bm::ENGRAM_MAX_TABLES);
+  if (!tables || !n_rows) return fail(BITMOE_EINVAL, "%s: tables or n_rows is NULL", fn);
+  if (n_groups < 0 || per < 1) return fail(BITMOE_EINVAL, "%s: n_groups=%lld per=%d", fn, (long long)n_groups, per);
+  bm::EngramTables tabs{};
+  tabs.n = n_tables;
+  for (int j = 0; j < n_tables; ++j) {
+    if (n_rows[j] < 0) return fail(BITMOE_EINVAL, "%s: n_rows[%d]=%lld is negative", fn, j, (long long)n_rows[j]);
+    if (!tables[j] || !aligned(tables[j], 8))
+      return fail(BITMOE_EINVAL, "%s: tables[%d] is NULL or not 8-byte aligned", fn, j);
+    tabs.table[j] = tables[j];
+    tabs.rows[j] = n_rows[j];
+  }
+  if (n_groups > ((int64_t(1) << 33) / n_tables / per))
+    return fail(BITMOE_EUNSUPPORTED, "%s: %lld groups of %d x %d rows in one call", fn, (long long)n_groups, n_tables,
+                per);
+  const int64_t n = n_groups * n_tables * per;
+  if (n == 0) return BITMOE_OK;
+  if (!row_ids || !aligned(row_ids, 8)) return fail(BITMOE_EINVAL, "%s: row_ids is NULL or not 8-byte aligned", fn);
+  if (!out || !aligned(out, 16)) return fail(BITMOE_EINVAL, "%s: out is NULL or not 16-byte aligned", fn);
+  if (status && !aligned(status, 8)) return fail(BITMOE_EINVAL, "%s: status not 8-byte aligned", fn);
+  hipError_t e = bm::launch_engram_gather(tabs, per, row_ids, n, out, status, stream);
   if (e != hipSuccess) return hip_fail(fn, e);
   return BITMOE_OK;
 }

@@ -24,7 +24,15 @@ void prof_events(const char *name, hipEvent_t *start, hipEvent_t *stop);
       hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                              \
   } while (0)
 
-hipError_t launch_engram_gather(const uint8_t *table, int64_t n_rows, const int64_t *row_ids, int64_t n,
+// Engram tables of one gather launch (up to four; by value as a kernel argument)
+constexpr int ENGRAM_MAX_TABLES = 4;
+struct EngramTables {
+  const uint8_t *table[ENGRAM_MAX_TABLES];
+  int64_t rows[ENGRAM_MAX_TABLES];
+  int32_t n;
+};
+// id i of row_ids reads tabs.table[(i / per) % tabs.n]
+hipError_t launch_engram_gather(const EngramTables &tabs, int32_t per, const int64_t *row_ids, int64_t n,
                                 uint16_t *out, int64_t *status, hipStream_t stream);
 // kv: [T][5 W] float32 scratch
 hipError_t launch_engram_inject(const uint16_t *rows, int T, int n_rows, const uint16_t *w_kv, int W,

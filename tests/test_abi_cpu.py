@@ -171,6 +171,26 @@ def test_layer_residual_rejects_bad_args(lib):
     assert lib.moe_layer_residual(*args(T=0, xn=None)) == bm.OK
 
 
+def test_engram_gather_tables_rejects_bad_args(lib):
+    P = ctypes.c_void_p
+    tabs = (ctypes.c_void_p * 2)(0x10000, 0x20000)
+    rows = (ctypes.c_int64 * 2)(1 << 22, 1 << 22)
+    call = lambda t=tabs, r=rows, nt=2, ids=P(0x30000), g=5, per=8, out=P(0x40000), st=None: \
+        lib.engram_gather_tables(t, r, nt, ids, g, per, out, st, None)
+    assert call(nt=0) == bm.EINVAL
+    assert call(nt=5) == bm.EINVAL
+    assert call(t=None) == bm.EINVAL
+    assert call(t=(ctypes.c_void_p * 2)(0x10000, 0x20004)) == bm.EINVAL  # table 1 not 8-byte aligned
+    assert call(r=(ctypes.c_int64 * 2)(1, -1)) == bm.EINVAL
+    assert call(per=0) == bm.EINVAL
+    assert call(g=-1) == bm.EINVAL
+    assert call(ids=None) == bm.EINVAL
+    assert call(out=P(0x40008)) == bm.EINVAL
+    assert call(st=P(0x50004)) == bm.EINVAL
+    assert call(g=1 << 40) == bm.EUNSUPPORTED
+    assert call(g=0, ids=None, out=None) == bm.OK
+
+
 def test_int8_mode_workspace_and_shape_limits(lib):
     L = _layer()
     n8, n1 = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -61,6 +61,57 @@ def test_engram_verify_tables_and_hashed_rows():
     assert np.array_equal(dev, synthdata.engram_rows(keys[0], sample))
 
 
+def test_engram_gather_tables_verify_batch():
+    # both tables of a verify batch in one launch: the oracle's rows, and the
+    # two single-table calls' rows, bit for bit
+    cfg = synthdata.CONFIGS["verify"]
+    n_rows = synthdata.ENGRAM_ROWS
+    lut = lut_device()
+    keys = [synthdata.tensor_key(1, synthdata.KIND_ENGRAM, tb) for tb in range(2)]
+    tables = []
+    for key in keys:
+        t = torch.empty(n_rows * 264, dtype=torch.uint8, device="cuda")
+        bm.fill(t, key, bm.FILL_ENGRAM, lut)
+        tables.append(t.view(n_rows, 264))
+    toks = synthdata.token_ids(1, 3, cfg.history + cfg.T)
+    ids = synthdata.engram_row_ids(1, toks, cfg.history)  # [T][2][8]
+    out = _bits(bm.engram_gather_tables(tables, torch.from_numpy(ids.copy()).cuda()))
+    assert out.shape == (cfg.T, 2, 8, 256)
+    for tb in range(2):
+        ref = engram.gather(lambda r, k=keys[tb]: synthdata.engram_rows(k, r), n_rows, ids[:, tb, :])
+        assert compare.bf16_bits_equal(out[:, tb], ref)
+        single = _bits(bm.engram_gather(tables[tb], torch.from_numpy(ids[:, tb, :].copy()).cuda()))
+        assert np.array_equal(out[:, tb], single)
+
+
+def test_engram_gather_tables_bad_ids_and_sizes():
+    # three tables of different row counts; an id valid in one table and out of
+    # range in another is zero-filled there and recorded with its flat index
+    rng = np.random.default_rng(4)
+    host = []
+    for n in (5, 9, 3):
+        r = rng.integers(0, 256, (n, 264), dtype=np.uint8)
+        r[:, 256:] = rng.integers(110, 140, (n, 8), dtype=np.uint8)
+        host.append(r)
+    tables = [torch.from_numpy(r).cuda() for r in host]
+    ids = np.array([[[0, 4], [8, 1], [2, 0]],
+                    [[4, 3], [5, 6], [3, -1]]], dtype=np.int64)  # [2 groups][3 tables][2]
+    status = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out = _bits(bm.engram_gather_tables(tables, torch.from_numpy(ids).cuda(), status=status))
+    for g in range(2):
+        for j in range(3):
+            for s in range(2):
+                i = ids[g, j, s]
+                if 0 <= i < host[j].shape[0]:
+                    assert compare.bf16_bits_equal(out[g, j, s][None], engram.decode_rows(host[j][[i]]))
+                else:
+                    assert np.all(out[g, j, s] == 0)
+    code, detail = bm.read_status(status)
+    assert code == bm.DEV_BAD_ROW and detail == 10  # group 1, table 2, slot 0: 3 >= 3 rows
+    empty = bm.engram_gather_tables(tables, torch.zeros((0, 3, 2), dtype=torch.int64, device="cuda"))
+    assert empty.shape == (0, 3, 2, 256)
+
+
 def test_engram_bad_ids_zero_fill_and_status():
     rows = np.random.default_rng(0).integers(0, 256, (10, 264), dtype=np.uint8)
     rows[:, 256:] = 120
