@@ -54,8 +54,21 @@ struct GeoI8 {
   static constexpr int BUF = 16 * MT * ROWB;         // bytes of one activation buffer
   static constexpr int SBUF = 16 * MT * SUMS * 2;    // bytes of one sums buffer
   static constexpr int DBUF = 16 * MT * DXN * 4;     // bytes of one scales buffer
-  static constexpr int ROWS_OFF = 2 * (BUF + SBUF + DBUF);
+  // gate/up stages one step's weights per matrix in LDS, as the bf16 kernel
+  // does: bytes 0..79 of every row's super-block as 5 16-byte pieces per row,
+  // then the rows' d|dmin words.  Down loads each lane's bytes into registers.
+  static constexpr bool WLDS = GATEUP;
+  static constexpr int WMAT = BN * 84;               // bytes per matrix and step
+  static constexpr int WBUF = WLDS ? NM * WMAT : 0;
+  static constexpr int WX4 = BN * 5 / 64;            // 64-lane 16-byte copies per matrix and step
+  static constexpr int WX1 = BN / 64;                // 64-lane dword copies (d|dmin) per matrix and step
+  static constexpr int WPM = WAVES / NM;             // waves copying one matrix
+  static constexpr int WC4 = (WX4 + WPM - 1) / WPM;  // 16-byte copies per wave and step
+  static constexpr int WC1 = (WX1 + WPM - 1) / WPM;  // dword copies per wave and step
+  static constexpr int ROWS_OFF = 2 * (BUF + SBUF + DBUF) + 2 * WBUF;
   static constexpr size_t SMEM = size_t(ROWS_OFF) + 16 * MT * 4;
+  static_assert(BN * 5 % 64 == 0 && BN % 64 == 0 && WAVES % NM == 0, "weight copies of whole 64-lane rows");
+  static_assert(SMEM <= 160 * 1024, "LDS of one CU");
 };
 
 // One lane's bytes of a super-block: 8 code bytes of each half, the 16 scale
@@ -171,6 +184,7 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
   uint8_t *abuf = smem;
   uint8_t *sbuf = smem + 2 * Gm::BUF;
   uint8_t *dbuf = sbuf + 2 * Gm::SBUF;
+  uint8_t *wbuf = dbuf + 2 * Gm::DBUF;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, nl = lane & 15;
   const int nsteps = g.K / KS;
@@ -179,6 +193,23 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
   const uint8_t *wb[NM];
   wb[0] = g.b0 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
   if constexpr (GATEUP) wb[1] = g.b1 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
+  // weight copies (gate/up): wave `wave` copies matrix wm; its 16-byte copy c
+  // moves pieces 64 j + l (lane l, j = wj0 + WPM c) of the step image, piece i
+  // being bytes 16 (i % 5) .. +15 of row i / 5's super-block; its dword copy
+  // moves the d|dmin words of rows 64 j + l.  The source offsets (from the
+  // block's first row, step 0) do not depend on the step.
+  const int wm = wave / Gm::WPM, wj0 = wave % Gm::WPM;
+  const uint8_t *wsrc = (wm ? g.b1 : g.b0) + size_t(e) * g.b_stride + size_t(ntile) * Gm::BN * row_bytes;
+  uint32_t woff4[Gm::WC4], woff1[Gm::WC1];
+#pragma unroll
+  for (int c = 0; c < Gm::WC4; ++c) {
+    const int i = 64 * min(wj0 + Gm::WPM * c, Gm::WX4 - 1) + lane;
+    const int row = i / 5;
+    woff4[c] = uint32_t(row) * uint32_t(row_bytes) + 16u * uint32_t(i - 5 * row);
+  }
+#pragma unroll
+  for (int c = 0; c < Gm::WC1; ++c)
+    woff1[c] = uint32_t(64 * min(wj0 + Gm::WPM * c, Gm::WX1 - 1) + lane) * uint32_t(row_bytes) + 80u;
   // copies of step kb into buffer half: activation rows (256 B: 16 lanes, one
   // row per instruction so that the rows keep their padded LDS stride), their
   // stored sums (64 B: 4 lanes per row) and block scales (32 B: 2 lanes per row)
@@ -202,6 +233,37 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
                     lds_offset(dbuf + half * Gm::DBUF + 16 * b0));
       }
     }
+    if constexpr (!Gm::WLDS) return;
+    uint8_t *wd = wbuf + half * Gm::WBUF + wm * Gm::WMAT;
+    const uint8_t *ws = wsrc + size_t(kb) * 84;
+#pragma unroll
+    for (int c = 0; c < Gm::WC4; ++c) {
+      const int j = wj0 + Gm::WPM * c;
+      if (Gm::WX4 % Gm::WPM == 0 || j < Gm::WX4) lds_dma16(ws + woff4[c], lds_offset(wd + 1024 * j));
+    }
+#pragma unroll
+    for (int c = 0; c < Gm::WC1; ++c) {
+      const int j = wj0 + Gm::WPM * c;
+      if (Gm::WX1 % Gm::WPM == 0 || j < Gm::WX1) lds_dma4(ws + woff1[c], lds_offset(wd + Gm::BN * 80 + 256 * j));
+    }
+  };
+  // this lane's bytes of group ng, matrix m from the step image (the layout of q2i8_load)
+  auto read_b = [&](int half, Q2RawI8 (&raw)[NG][NM]) {
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint8_t *wm_ = wbuf + half * Gm::WBUF + m * Gm::WMAT;
+        const int r = wave * 16 * NG + 16 * ng + nl;
+        const uint8_t *sb = wm_ + 80 * r;
+        const int o = 16 + 16 * (gq >> 1) + 8 * (gq & 1);
+        const i8u32x2 h0 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o);
+        const i8u32x2 h1 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o + 32);
+        const i8u32x4 sc = *reinterpret_cast<const i8u32x4 *>(sb);
+        raw[ng][m].q[0] = h0.x, raw[ng][m].q[1] = h0.y, raw[ng][m].q[2] = h1.x, raw[ng][m].q[3] = h1.y;
+        raw[ng][m].sc[0] = sc.x, raw[ng][m].sc[1] = sc.y, raw[ng][m].sc[2] = sc.z, raw[ng][m].sc[3] = sc.w;
+        raw[ng][m].dd = *reinterpret_cast<const uint32_t *>(wm_ + Gm::BN * 80 + 4 * r);
+      }
   };
   auto load_b = [&](int kb, Q2RawI8 (&raw)[NG][NM]) {
 #pragma unroll
@@ -220,20 +282,23 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
       for (int m = 0; m < NM; ++m) acc[mi][ng][m] = zero;
   Q2RawI8 cur[NG][NM];
   issue(0, 0);
-  load_b(0, cur);
+  if constexpr (!Gm::WLDS) load_b(0, cur);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (!Gm::WLDS) {
 #pragma unroll
-  for (int ng = 0; ng < NG; ++ng)
+    for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-    for (int m = 0; m < NM; ++m) q2i8_settle(cur[ng][m]);
+      for (int m = 0; m < NM; ++m) q2i8_settle(cur[ng][m]);
+  }
   __syncthreads();
   for (int kb = 0; kb < nsteps; ++kb) {
     const int half = kb & 1;
     Q2RawI8 nxt[NG][NM];
     if (kb + 1 < nsteps) {
       issue(kb + 1, half ^ 1);
-      load_b(kb + 1, nxt);
+      if constexpr (!Gm::WLDS) load_b(kb + 1, nxt);
     }
+    if constexpr (Gm::WLDS) read_b(half, cur);
     const int8_t *Ab = reinterpret_cast<const int8_t *>(abuf + half * Gm::BUF);
     const uint16_t *Sx = reinterpret_cast<const uint16_t *>(sbuf + half * Gm::SBUF);
     const float *Dx = reinterpret_cast<const float *>(dbuf + half * Gm::DBUF);
@@ -300,13 +365,15 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
     if (kb + 1 < nsteps) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows, sums, scales and weight bytes have landed
       __syncthreads();                                  // ... and this step's buffers are no longer read
+      if constexpr (!Gm::WLDS) {
 #pragma unroll
-      for (int ng = 0; ng < NG; ++ng)
+        for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          q2i8_settle(nxt[ng][m]);
-          cur[ng][m] = nxt[ng][m];
-        }
+          for (int m = 0; m < NM; ++m) {
+            q2i8_settle(nxt[ng][m]);
+            cur[ng][m] = nxt[ng][m];
+          }
+      }
     }
   }
   // epilogue: lane holds rows 16 mi + 4 gq + r of column n_w + 16 ng
