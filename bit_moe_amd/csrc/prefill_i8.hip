@@ -26,8 +26,9 @@
 //
 // Blocking, plan and staging are those of the bf16 grouped GEMM
 // (prefill_q2.hip): chunks of up to 48 tokens (gate/up) or 32 pairs (down) of
-// one expert x 128 weight rows per block (8 waves x 16 rows), activation rows, their block scales
-// and stored sums staged in LDS one K-step ahead with direct-to-LDS copies.
+// one expert x 128 weight rows per block (8 waves x 16 rows); activation rows, their block
+// scales and stored sums, and the step's weight bytes (both matrices of gate/up) staged in LDS
+// one K-step ahead with direct-to-LDS copies.
 #include "common.h"
 #include "internal.h"
 #include "mfma_q2.h"
@@ -54,12 +55,12 @@ struct GeoI8 {
   static constexpr int BUF = 16 * MT * ROWB;         // bytes of one activation buffer
   static constexpr int SBUF = 16 * MT * SUMS * 2;    // bytes of one sums buffer
   static constexpr int DBUF = 16 * MT * DXN * 4;     // bytes of one scales buffer
-  // gate/up stages one step's weights per matrix in LDS, as the bf16 kernel
-  // does: bytes 0..79 of every row's super-block as 5 16-byte pieces per row,
-  // then the rows' d|dmin words.  Down loads each lane's bytes into registers.
-  static constexpr bool WLDS = GATEUP;
+  // Each step's weights are staged per matrix in LDS, as the bf16 gate/up
+  // kernel does: bytes 0..79 of every row's super-block as 5 16-byte pieces
+  // per row, then the rows' d|dmin words (one int8 activation part leaves the
+  // LDS room for it in down too).
   static constexpr int WMAT = BN * 84;               // bytes per matrix and step
-  static constexpr int WBUF = WLDS ? NM * WMAT : 0;
+  static constexpr int WBUF = NM * WMAT;
   static constexpr int WX4 = BN * 5 / 64;            // 64-lane 16-byte copies per matrix and step
   static constexpr int WX1 = BN / 64;                // 64-lane dword copies (d|dmin) per matrix and step
   static constexpr int WPM = WAVES / NM;             // waves copying one matrix
@@ -79,28 +80,10 @@ struct Q2RawI8 {
   uint32_t dd;
 };
 
-// super-blocks are 84 bytes: 4-byte alignment only
+// the step image in LDS holds 80 bytes per row: the code bytes of a lane group
+// start 8-byte aligned, the scale bytes 16-byte aligned
 typedef uint32_t i8u32x2 __attribute__((ext_vector_type(2)));
-typedef i8u32x2 __attribute__((aligned(4))) i8u32x2_a4;
 typedef uint32_t i8u32x4 __attribute__((ext_vector_type(4)));
-typedef i8u32x4 __attribute__((aligned(4))) i8u32x4_a4;
-
-BM_DEVICE Q2RawI8 q2i8_load(const uint8_t *sb, int g) {
-  Q2RawI8 r;
-  const int o = 16 + 16 * (g >> 1) + 8 * (g & 1);
-  const i8u32x2 h0 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o);
-  const i8u32x2 h1 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o + 32);
-  r.q[0] = h0.x, r.q[1] = h0.y, r.q[2] = h1.x, r.q[3] = h1.y;
-  const i8u32x4 s = *reinterpret_cast<const i8u32x4_a4 *>(sb);
-  r.sc[0] = s.x, r.sc[1] = s.y, r.sc[2] = s.z, r.sc[3] = s.w;
-  r.dd = *reinterpret_cast<const uint32_t *>(sb + 80);
-  return r;
-}
-
-BM_DEVICE void q2i8_settle(Q2RawI8 &r) {
-  asm volatile("" : "+v"(r.q[0]), "+v"(r.q[1]), "+v"(r.q[2]), "+v"(r.q[3]));
-  asm volatile("" : "+v"(r.sc[0]), "+v"(r.sc[1]), "+v"(r.sc[2]), "+v"(r.sc[3]), "+v"(r.dd));
-}
 
 // One half (h) of a lane's super-block bytes: its 8 code bytes and the scale
 // bytes of sub-blocks 8h .. 8h + 7.
@@ -190,10 +173,7 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
   const int nsteps = g.K / KS;
   const size_t row_bytes = size_t(nsteps) * 84;
   const int n_w = ntile * Gm::BN + wave * 16 * NG + nl;  // weight row of group 0; group ng adds 16 ng
-  const uint8_t *wb[NM];
-  wb[0] = g.b0 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
-  if constexpr (GATEUP) wb[1] = g.b1 + size_t(e) * g.b_stride + size_t(n_w) * row_bytes;
-  // weight copies (gate/up): wave `wave` copies matrix wm; its 16-byte copy c
+  // weight copies: wave `wave` copies matrix wm; its 16-byte copy c
   // moves pieces 64 j + l (lane l, j = wj0 + WPM c) of the step image, piece i
   // being bytes 16 (i % 5) .. +15 of row i / 5's super-block; its dword copy
   // moves the d|dmin words of rows 64 j + l.  The source offsets (from the
@@ -233,7 +213,6 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
                     lds_offset(dbuf + half * Gm::DBUF + 16 * b0));
       }
     }
-    if constexpr (!Gm::WLDS) return;
     uint8_t *wd = wbuf + half * Gm::WBUF + wm * Gm::WMAT;
     const uint8_t *ws = wsrc + size_t(kb) * 84;
 #pragma unroll
@@ -247,7 +226,9 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
       if (Gm::WX1 % Gm::WPM == 0 || j < Gm::WX1) lds_dma4(ws + woff1[c], lds_offset(wd + Gm::BN * 80 + 256 * j));
     }
   };
-  // this lane's bytes of group ng, matrix m from the step image (the layout of q2i8_load)
+  // this lane's bytes of group ng, matrix m from the step image: lane group gq
+  // reads code bytes 16 + 16 (gq / 2) + 8 (gq % 2) .. +7 of each half, the 16
+  // scale bytes and d|dmin of its row's super-block
   auto read_b = [&](int half, Q2RawI8 (&raw)[NG][NM]) {
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng)
@@ -257,19 +238,13 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
         const int r = wave * 16 * NG + 16 * ng + nl;
         const uint8_t *sb = wm_ + 80 * r;
         const int o = 16 + 16 * (gq >> 1) + 8 * (gq & 1);
-        const i8u32x2 h0 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o);
-        const i8u32x2 h1 = *reinterpret_cast<const i8u32x2_a4 *>(sb + o + 32);
+        const i8u32x2 h0 = *reinterpret_cast<const i8u32x2 *>(sb + o);
+        const i8u32x2 h1 = *reinterpret_cast<const i8u32x2 *>(sb + o + 32);
         const i8u32x4 sc = *reinterpret_cast<const i8u32x4 *>(sb);
         raw[ng][m].q[0] = h0.x, raw[ng][m].q[1] = h0.y, raw[ng][m].q[2] = h1.x, raw[ng][m].q[3] = h1.y;
         raw[ng][m].sc[0] = sc.x, raw[ng][m].sc[1] = sc.y, raw[ng][m].sc[2] = sc.z, raw[ng][m].sc[3] = sc.w;
         raw[ng][m].dd = *reinterpret_cast<const uint32_t *>(wm_ + Gm::BN * 80 + 4 * r);
       }
-  };
-  auto load_b = [&](int kb, Q2RawI8 (&raw)[NG][NM]) {
-#pragma unroll
-    for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) raw[ng][m] = q2i8_load(wb[m] + size_t(16 * ng) * row_bytes + size_t(kb) * 84, gq);
   };
   f32x4_t acc[NT][NG][NM];
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -282,23 +257,12 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
       for (int m = 0; m < NM; ++m) acc[mi][ng][m] = zero;
   Q2RawI8 cur[NG][NM];
   issue(0, 0);
-  if constexpr (!Gm::WLDS) load_b(0, cur);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if constexpr (!Gm::WLDS) {
-#pragma unroll
-    for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) q2i8_settle(cur[ng][m]);
-  }
   __syncthreads();
   for (int kb = 0; kb < nsteps; ++kb) {
     const int half = kb & 1;
-    Q2RawI8 nxt[NG][NM];
-    if (kb + 1 < nsteps) {
-      issue(kb + 1, half ^ 1);
-      if constexpr (!Gm::WLDS) load_b(kb + 1, nxt);
-    }
-    if constexpr (Gm::WLDS) read_b(half, cur);
+    if (kb + 1 < nsteps) issue(kb + 1, half ^ 1);
+    read_b(half, cur);
     const int8_t *Ab = reinterpret_cast<const int8_t *>(abuf + half * Gm::BUF);
     const uint16_t *Sx = reinterpret_cast<const uint16_t *>(sbuf + half * Gm::SBUF);
     const float *Dx = reinterpret_cast<const float *>(dbuf + half * Gm::DBUF);
@@ -365,15 +329,6 @@ BM_DEVICE void group_i8_body(const GroupI8Args &g, int e, int valid, int base, i
     if (kb + 1 < nsteps) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // step kb+1's rows, sums, scales and weight bytes have landed
       __syncthreads();                                  // ... and this step's buffers are no longer read
-      if constexpr (!Gm::WLDS) {
-#pragma unroll
-        for (int ng = 0; ng < NG; ++ng)
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            q2i8_settle(nxt[ng][m]);
-            cur[ng][m] = nxt[ng][m];
-          }
-      }
     }
   }
   // epilogue: lane holds rows 16 mi + 4 gq + r of column n_w + 16 ng
