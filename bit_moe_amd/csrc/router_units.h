@@ -100,7 +100,11 @@ BM_DEVICE void topk_token(const float *L, int E, int k, int32_t *ids, float *wts
   for (int i = 0; i < PER; ++i) key[i] = lane + 64 * i < E ? logit_key(lv[i]) : 0u;
   float sel_v[8];
   int sel_i[8];
-  for (int j = 0; j < k; ++j) {
+  // unrolled to the largest k, so that every round writes its selection to a
+  // fixed register (a run-time index would cost a select chain per round)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
     uint32_t m = key[0];
     int s = 0;
 #pragma unroll
